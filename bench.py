@@ -1,0 +1,262 @@
+"""Benchmark of one paged DSA layer step on one MI355X.
+
+A step is the whole hot path over one batch: indexer scores -> top-k ->
+GQA sparse attention (split over the k slots) -> log-sum-exp merge, four
+library calls on one stream. The default workload is batch 64 decode at
+context 32768, page 64, 64 query / 8 KV heads of dim 128, indexer 64 x 128,
+top-k 2048, bf16, synthetic inputs drawn on the device (randomly permuted
+page tables). Inputs are resident in HBM before the timed region; W warm-up
+steps run untimed, then K steps are timed between two synchronizations.
+
+Prints one JSON line:
+  value          layer latency in microseconds (lower is better)
+  hbm_gbps       algorithmic bytes of the layer / latency
+  roofline       the dominant kernel's algorithmic bytes per launch / its
+                 average duration (HIP events on the launch stream), against
+                 8 TB/s
+  cpu_baseline   the CPU oracle timed on a bounded sample of rows of the same
+                 workload, extrapolated to the whole layer
+"""
+
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "DSA layer latency (us) + HBM GB/s, B=64 ctx 32k top-k 2048, 1 GPU"
+HBM_PEAK_GBPS = 8000.0
+PAGES_LAYER_US = 160.0  # one decode layer, batch 64, 32K context, top-k 2048, on GB300 (context)
+
+
+def algorithmic_bytes(wl, row_len):
+    """Bytes the method itself must move, per kernel, summed over rows:
+    indexer: keys L*D_I*e, qI H_I*D_I*e, w 4*H_I, score write 4*L, block table 4*ceil(L/P)
+    top-k:   score read 4*L, index write 4*k
+    attention: K and V of the k_eff selected keys k_eff*Hkv*d*e*2, q Hq*d*e,
+               index read 4*k, block table 4*ceil(L/P)
+    merge:   output write Hq*d*e
+    (split partials are overhead, not counted)."""
+    e = 2 if wl.dtype == "bf16" else 4
+    b = {"indexer": 0, "topk": 0, "attention": 0, "merge": 0}
+    for L in (int(x) for x in row_len):
+        pages = -(-L // wl.page)
+        k_eff = min(wl.topk, L)
+        b["indexer"] += L * wl.di * e + wl.hi * wl.di * e + 4 * wl.hi + 4 * L + 4 * pages
+        b["topk"] += 4 * L + 4 * wl.topk
+        b["attention"] += k_eff * wl.hkv * wl.d * e * 2 + wl.hq * wl.d * e + 4 * wl.topk + 4 * pages
+        b["merge"] += wl.hq * wl.d * e
+    return b
+
+
+def _events(torch):
+    return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+
+
+def time_steps(step, steps, warmup, torch):
+    for _ in range(warmup):
+        step.run()
+    torch.cuda.synchronize()
+    a, b = _events(torch)
+    a.record()
+    for _ in range(steps):
+        step.run()
+    b.record()
+    torch.cuda.synchronize()
+    return a.elapsed_time(b) / steps  # ms
+
+
+def time_kernels(step, steps, torch):
+    """Average duration of each stage's kernel, HIP events on the launch stream."""
+    stages = [("indexer", step.indexer), ("topk", step.topk), ("attention", step.attention),
+              ("merge", step.merge)]
+    evs = {n: [_events(torch) for _ in range(steps)] for n, _ in stages}
+    for i in range(steps):
+        for n, fn in stages:
+            evs[n][i][0].record()
+            fn()
+            evs[n][i][1].record()
+    torch.cuda.synchronize()
+    return {n: 1000.0 * sum(a.elapsed_time(b) for a, b in evs[n]) / steps for n, _ in stages}
+
+
+def cpu_baseline(step, budget_s, torch):
+    """The oracle, as it stands, on a bounded sample of rows of this workload."""
+    import numpy as np
+
+    from oracle import dsa_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    inp, wl = step.inp, step.wl
+    dev = inp.q.device
+
+    def host(t):
+        return t.detach().to("cpu", torch.float64).numpy()
+
+    rng = np.random.default_rng(0)
+    order = rng.permutation(step.rows)
+    spent, rows_done, row_lens = 0.0, [], []
+    for r in order.tolist():
+        L = int(step.row_len_host[r])
+        req = int(step.row_req_host[r])
+        bt = inp.block_table[req]
+        pos = torch.arange(L, device=dev)
+        kI = host(inp.kI_cache[bt[pos // wl.page].long(), pos % wl.page])
+        qI, w, q = host(inp.qI[r]), host(inp.w[r]), host(inp.q[r])
+        t0 = time.perf_counter()
+        s = O.indexer_scores_row(qI, w, kI)
+        idx = O.topk_row(s, L, wl.topk)
+        t1 = time.perf_counter()
+        sel = idx[idx >= 0]
+        n = len(sel)
+        kc = np.zeros((wl.topk, 1, wl.hkv, wl.d))
+        vc = np.zeros((wl.topk, 1, wl.hkv, wl.d))
+        p = torch.from_numpy(sel.astype(np.int64)).to(dev)
+        pages = bt[p // wl.page].long()
+        kc[:n, 0] = host(inp.k_cache[pages, p % wl.page])
+        vc[:n, 0] = host(inp.v_cache[pages, p % wl.page])
+        local = np.full(wl.topk, -1, np.int64)
+        local[:n] = np.arange(n)
+        t2 = time.perf_counter()
+        po, pl = O.attention_split_row(q, kc, vc, np.arange(wl.topk), 1, local, wl.attn_scale,
+                                       step.num_splits)
+        O.merge_row(po, pl)
+        t3 = time.perf_counter()
+        spent += (t1 - t0) + (t3 - t2)
+        rows_done.append(r)
+        row_lens.append(L)
+        if spent >= budget_s:
+            break
+    # scale by row length share so ragged samples extrapolate fairly
+    total_len = float(sum(int(x) for x in step.row_len_host))
+    share = sum(row_lens) / total_len if total_len else 1.0
+    est_s = spent / share if share > 0 else spent
+    return {
+        "value": round(est_s * 1e6, 1),
+        "unit": "us",
+        "cores": int(threads),
+        "kind": "oracle",
+        "sample": (f"{len(rows_done)} of {step.rows} rows (full indexer + top-k + attention + "
+                   f"merge each, float64 NumPy), {spent:.1f} s, scaled by their share of the "
+                   f"layer's keys ({share:.4f}); gathers and host copies not timed"),
+    }
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--workload", default="headline",
+                    help="headline (default), decode, tiny, ragged or mixed")
+    ap.add_argument("--splits", type=int, default=0, help="attention splits (0 = default)")
+    ap.add_argument("--block-rows", type=int, default=1, help="rows per indexer score block")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="oracle time budget for cpu_baseline (0 = skip)")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="instead of the step, run a plain device copy of this many MiB "
+                         "(calibrates HBM byte counters)")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(requests shard across GPUs with no exchange; see the design notes)",
+              file=sys.stderr)
+        return 2
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib << 20
+        src = torch.empty(n // 4, dtype=torch.float32, device="cuda").fill_(1.0)
+        dst = torch.empty_like(src)
+        for _ in range(args.warmup + args.steps):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": n, "launches": args.warmup + args.steps}))
+        return 0
+
+    from sparse_attention_decode_02_amd import inputs as I
+    from sparse_attention_decode_02_amd.step import DsaStep
+
+    wl = I.WORKLOADS[args.workload]()
+    print(f"[bench] generating {wl.name} on the device", file=sys.stderr, flush=True)
+    inp = I.generate(wl, "cuda")
+    step = DsaStep(inp, num_splits=args.splits or None, block_rows=args.block_rows)
+    torch.cuda.synchronize()
+    print(f"[bench] rows {step.rows} width {step.width} splits {step.num_splits}",
+          file=sys.stderr, flush=True)
+
+    ms = time_steps(step, args.steps, args.warmup, torch)
+    kern = time_kernels(step, args.steps, torch)
+    layer_us = ms * 1000.0
+    ab = algorithmic_bytes(wl, step.row_len_host)
+    total_bytes = sum(ab.values())
+    gbps = total_bytes / (layer_us * 1e-6) / 1e9
+    dominant = max(("indexer", "attention"), key=lambda n: kern[n])
+    dom_gbps = ab[dominant] / (kern[dominant] * 1e-6) / 1e9
+    print(f"[bench] layer {layer_us:.1f} us, {gbps:.0f} GB/s; kernels (us) "
+          + ", ".join(f"{n} {v:.1f}" for n, v in kern.items()), file=sys.stderr, flush=True)
+
+    result = {
+        "metric": METRIC,
+        "value": round(layer_us, 2),
+        "unit": "us",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms, 5),
+        "higher_is_better": False,
+        "scaling": "weak",
+        "vs_baseline": round(layer_us / PAGES_LAYER_US, 4) if args.workload == "headline" else None,
+        "dtype": "bf16" if wl.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": wl.name,
+            "batch_rows": step.rows,
+            "context": int(max(step.row_len_host)),
+            "topk": wl.topk,
+            "page": wl.page,
+            "q_heads": wl.hq,
+            "kv_heads": wl.hkv,
+            "head_dim": wl.d,
+            "indexer": f"{wl.hi}x{wl.di}",
+            "attention_splits": step.num_splits,
+            "indexer_block_rows": args.block_rows,
+        },
+        "hbm_gbps": round(gbps, 1),
+        "layer_frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "algorithmic_bytes": total_bytes,
+        "kernels_us": {n: round(v, 2) for n, v in kern.items()},
+        "roofline": {
+            "kernel": dominant,
+            "bound": "hbm",
+            "achieved": round(dom_gbps, 1),
+            "peak": HBM_PEAK_GBPS,
+            "unit": "GB/s",
+            "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
+            "traffic": None,
+            "algorithmic_bytes_per_launch": ab[dominant],
+        },
+    }
+    if args.cpu_seconds > 0:
+        result["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds, torch)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

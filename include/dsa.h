@@ -1,0 +1,227 @@
+/*
+ * dsa.h -- C ABI of libdsa.so, the MI355X (gfx950) paged DeepSeek-sparse-
+ * attention step:
+ *
+ *   indexer scores -> length-bounded exact top-k -> GQA sparse attention
+ *   split over the k slots -> log-sum-exp merge
+ *
+ * The method is the one of Megatron-LM pull request 7211 ("native dynamic
+ * inference for simplified DSA over GQA"); each entry point names the commit
+ * of that pull request whose message defines its operation.
+ *
+ * Conventions shared by every entry point
+ * ---------------------------------------
+ * - Pointers marked "device" are HIP device memory, dense row-major, owned by
+ *   the caller; the library never allocates, frees, synchronizes, or reads
+ *   device memory on the host. Pointers marked "host" are host memory.
+ * - "stream" is a hipStream_t (NULL = the default stream). All work is
+ *   enqueued on it in call order; the calls return before the work finishes.
+ * - Return value: DSA_OK (0) or a negative dsa_status. Every host-visible
+ *   argument is checked before anything is enqueued; on a negative status
+ *   nothing was launched and no output was written. DSA_ERR_LAUNCH reports a
+ *   failed kernel launch.
+ * - Device-resident metadata (block-table entries, row lengths, selected
+ *   positions, score blocks) is a caller contract and is not read on the
+ *   host: block_table[q][j] must name a valid page for every page a row of
+ *   request q reaches, row_len[r] must not exceed the score width or the
+ *   request's cached tokens, and every selected position must be -1 or lie in
+ *   [0, row_len[r]). Violations are undefined behaviour.
+ * - Per-step integers (rows, width, k, lengths, number of splits) are runtime
+ *   values, so the launch shape depends only on the call's arguments and the
+ *   kernels can be replayed with new lengths in the same buffers (commit
+ *   "Treat every query token of a step ... as a row": launch sizes depend only
+ *   on the padded batch; the PR description: graph replay with changing token
+ *   positions and active lengths).
+ * - The calls are thread-safe: the library keeps no mutable global state.
+ */
+#ifndef DSA_H
+#define DSA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DSA_F32 = 0,  /* IEEE float32 */
+  DSA_BF16 = 1  /* bfloat16 (upper half of a float32) */
+} dsa_dtype;
+
+typedef enum {
+  DSA_OK = 0,
+  DSA_ERR_NULL = -1,        /* a required pointer is NULL */
+  DSA_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
+  DSA_ERR_ALIGN = -3,       /* a device pointer is not 16-byte aligned */
+  DSA_ERR_UNSUPPORTED = -4, /* head count / head dim / dtype combination not built */
+  DSA_ERR_WORKSPACE = -5,   /* reserved */
+  DSA_ERR_LAUNCH = -6       /* the kernel launch failed */
+} dsa_status;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* dsa_status_string(int status);
+
+/* Version of this ABI (incremented on incompatible change). */
+int dsa_abi_version(void);
+
+/* ------------------------------------------------------------------------
+ * Row plan (host only; no HIP call)
+ *
+ * Commit "Treat every query token of a step, decode or prefill, as a row that
+ * routes to the top-k of its causal prefix": the rows of a step, and its
+ * score blocks (consecutive rows of one request scored against shared key
+ * tiles).
+ * ------------------------------------------------------------------------ */
+
+/*
+ * dsa_plan_rows: request q has prior[q] >= 0 tokens cached before the step
+ * and appends new_tokens[q] >= 0 tokens (1 = decode). Each new token is a
+ * row, request by request, in token order: row_req = q and row_len =
+ * prior[q] + i + 1 for its i-th new token (a row attends positions
+ * [0, row_len)). Writes *num_rows = sum(new_tokens) and the first *num_rows
+ * entries of row_req / row_len (host int32 arrays of max_rows entries).
+ * Errors: NULL pointer; num_reqs < 0, a negative count, a length that
+ * overflows int32, or more rows than max_rows -> DSA_ERR_SHAPE.
+ */
+int dsa_plan_rows(int num_reqs, const int32_t* prior, const int32_t* new_tokens, int max_rows,
+                  int32_t* row_req, int32_t* row_len, int* num_rows);
+
+/*
+ * dsa_plan_blocks: splits rows into score blocks, runs of at most
+ * max_rows_per_block consecutive rows with equal row_req. Writes
+ * (first_row, n_rows) pairs to blocks (host int32 [max_blocks][2]) and their
+ * count to *num_blocks. Errors: NULL pointer; rows < 0; max_rows_per_block
+ * < 1; more blocks than max_blocks -> DSA_ERR_SHAPE.
+ */
+int dsa_plan_blocks(int rows, const int32_t* row_req, int max_rows_per_block, int max_blocks,
+                    int32_t* blocks, int* num_blocks);
+
+/*
+ * dsa_score_width: the score buffer's row stride for these rows: the largest
+ * row_len rounded up to a multiple of 64 (at least 64). row_len is host
+ * memory. Errors: NULL pointer, rows < 0, a negative length.
+ */
+int dsa_score_width(int rows, const int32_t* row_len, int* width);
+
+/* ------------------------------------------------------------------------
+ * dsa_indexer_scores -- lightning-indexer scores.
+ *
+ * Commit "Replace the CuTe decode kernels with two Triton kernels": the
+ * indexer streams page-contiguous key tiles on the matrix cores, and each
+ * row is scored only up to its length. For row r of request q = row_req[r]
+ * and every position s < row_len[r]:
+ *
+ *   scores[r][s] = sum_h w[r][h] * max(0, sum_j q_idx[r][h][j] * kI[q][s][j])
+ *
+ * where kI[q][s] = k_idx_cache[block_table[q][s / page_size]][s % page_size].
+ * Positions [row_len[r], width) of the row are not written. -0.0 is written as
+ * +0.0. bf16 inputs are multiplied exactly and accumulated in fp32 on MFMA;
+ * fp32 inputs use fp32 FMA.
+ *
+ *   q_idx        device [rows][num_heads][head_dim]    dtype
+ *   w            device [rows][num_heads]               float32
+ *   k_idx_cache  device [num_pages][page_size][head_dim] dtype
+ *   block_table  device [num_reqs][max_pages]           int32
+ *   row_req      device [rows]                          int32
+ *   row_len      device [rows]                          int32
+ *   blocks       device [num_blocks][2] (first_row, n_rows) int32, or NULL
+ *                for one row per block; rows of a block share a request
+ *   scores       device [rows][width]                   float32 (output)
+ *
+ * Supported: bf16 with head_dim in {64, 128} and num_heads in {32, 64};
+ * fp32 with head_dim in {32, 64, 128} and 1 <= num_heads <= 64.
+ * page_size is a power of two; width is a positive multiple of 4; q_idx,
+ * k_idx_cache and scores are 16-byte aligned.
+ * ------------------------------------------------------------------------ */
+int dsa_indexer_scores(const void* q_idx, const float* w, const void* k_idx_cache,
+                       const int32_t* block_table, const int32_t* row_req, const int32_t* row_len,
+                       const int32_t* blocks, int num_blocks, float* scores, int rows, int width,
+                       int num_heads, int head_dim, int page_size, int max_pages, dsa_dtype dtype,
+                       void* stream);
+
+/* ------------------------------------------------------------------------
+ * dsa_topk -- length-bounded exact top-k.
+ *
+ * Commits "Replace the CuTe decode kernels with two Triton kernels" (the
+ * selection reads each row only up to its length), "When a step's context
+ * bound reaches 64K keys ..." (the result is the exact top k), and "Replace
+ * the Triton radix selector with torch.topk ..." (valid negative-infinity
+ * scores rank ahead of padding). For every row r with L = row_len[r]:
+ * selects the min(k, L) positions of [0, L) with the largest scores, ties to
+ * the lower position, -0.0 equal to +0.0, and writes them to idx[r] in
+ * ascending position order, followed by -1 in the remaining slots.
+ * NaN scores are outside the contract (never out-of-bounds, result
+ * unspecified).
+ *
+ *   scores   device [rows][width] float32, 16-byte aligned
+ *   row_len  device [rows] int32
+ *   idx      device [rows][k] int32 (output)
+ *
+ * 1 <= k <= width; width a positive multiple of 4.
+ * ------------------------------------------------------------------------ */
+int dsa_topk(const float* scores, const int32_t* row_len, int rows, int width, int k,
+             int32_t* idx, void* stream);
+
+/* ------------------------------------------------------------------------
+ * dsa_sparse_attn -- GQA sparse attention over split k-slot slices.
+ *
+ * Commit "Replace the CuTe decode kernels with two Triton kernels": one
+ * program serves all query heads of a KV group, reading each selected key and
+ * value once, and the top-k slots are split across programs; commit "Restore
+ * the upstream Blackwell FP32 probability reduction": probabilities stay fp32
+ * through the value reduction. Split s covers slots [s*c, min(k, (s+1)*c))
+ * with c = ceil(k / num_splits). For row r, query head h, KV head
+ * g = h / (num_q_heads / num_kv_heads), and the valid selected positions p_j
+ * (idx >= 0) of the split:
+ *
+ *   z_j = scale * q[r][h] . K[p_j][g],  m = max_j z_j,  l = sum_j exp(z_j - m)
+ *   part_o[r][h][s]   = sum_j exp(z_j - m) V[p_j][g] / l
+ *   part_lse[r][h][s] = m + ln l            (0 and -inf for an empty split)
+ *
+ * with K[p] = k_cache[block_table[q][p / page_size]][p % page_size] for the
+ * row's request q (V likewise).
+ *
+ *   q        device [rows][num_q_heads][head_dim]                 dtype
+ *   k_cache  device [num_pages][page_size][num_kv_heads][head_dim] dtype
+ *   v_cache  device, same layout as k_cache
+ *   block_table, row_req: as for dsa_indexer_scores
+ *   idx      device [rows][k] int32 (dsa_topk's output)
+ *   part_o   device [rows][num_q_heads][num_splits][head_dim] float32 (output)
+ *   part_lse device [rows][num_q_heads][num_splits] float32 (output)
+ *
+ * Supported: head_dim in {64, 128}; num_q_heads / num_kv_heads in
+ * {1, 2, 4, 8, 16}; 1 <= num_splits <= k; page_size a power of two; q,
+ * k_cache, v_cache and part_o 16-byte aligned.
+ * ------------------------------------------------------------------------ */
+int dsa_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_table, const int32_t* row_req, const int32_t* idx,
+                    int rows, int num_q_heads, int num_kv_heads, int head_dim, int k,
+                    int page_size, int max_pages, float scale, int num_splits, float* part_o,
+                    float* part_lse, dsa_dtype dtype, void* stream);
+
+/* ------------------------------------------------------------------------
+ * dsa_merge -- log-sum-exp merge of the split partials (flash decoding,
+ * commit "Replace the CuTe decode kernels with two Triton kernels").
+ * For each row r and head h, over the splits s:
+ *
+ *   M = max_s lse_s,  W = sum_s exp(lse_s - M),
+ *   out[r][h] = sum_s exp(lse_s - M) o_s / W,  out_lse[r][h] = M + ln W
+ *
+ * and out = 0, out_lse = -inf when every split is empty.
+ *
+ *   part_o, part_lse  device, as written by dsa_sparse_attn
+ *   out      device [rows][num_q_heads][head_dim] out_dtype (bf16 rounds to
+ *            nearest even) (output)
+ *   out_lse  device [rows][num_q_heads] float32 (output), or NULL
+ *
+ * 1 <= head_dim <= 256; num_splits >= 1; part_o and out 16-byte aligned.
+ * ------------------------------------------------------------------------ */
+int dsa_merge(const float* part_o, const float* part_lse, int rows, int num_q_heads, int head_dim,
+              int num_splits, void* out, float* out_lse, dsa_dtype out_dtype, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DSA_H */

@@ -1,0 +1,197 @@
+// C ABI of libdsa.so: host-side argument checks, row planning, and dispatch
+// to the HIP kernels. Every check runs before any launch, so a negative
+// status means nothing was enqueued and no output was touched. No entry
+// point allocates, frees, synchronizes, or reads device memory.
+
+#include <math.h>
+
+#include "../../include/dsa.h"
+#include "dsa_kernels.h"
+
+namespace {
+
+constexpr int kAbiVersion = 1;
+
+bool aligned(const void* p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+
+// log2 of a power of two in [1, 65536], else -1.
+int pow2_shift(int v) {
+  if (v < 1 || v > 65536 || (v & (v - 1)) != 0) return -1;
+  int s = 0;
+  while ((1 << s) != v) ++s;
+  return s;
+}
+
+int launch_status(hipError_t e) { return e == hipSuccess ? DSA_OK : DSA_ERR_LAUNCH; }
+
+}  // namespace
+
+extern "C" {
+
+const char* dsa_status_string(int status) {
+  switch (status) {
+    case DSA_OK: return "ok";
+    case DSA_ERR_NULL: return "a required pointer is NULL";
+    case DSA_ERR_SHAPE: return "a size is out of range or inconsistent";
+    case DSA_ERR_ALIGN: return "a device pointer is not 16-byte aligned";
+    case DSA_ERR_UNSUPPORTED: return "head count / head dim / dtype combination not supported";
+    case DSA_ERR_WORKSPACE: return "workspace too small";
+    case DSA_ERR_LAUNCH: return "kernel launch failed";
+    default: return "unknown status";
+  }
+}
+
+int dsa_abi_version(void) { return kAbiVersion; }
+
+int dsa_plan_rows(int num_reqs, const int32_t* prior, const int32_t* new_tokens, int max_rows,
+                  int32_t* row_req, int32_t* row_len, int* num_rows) {
+  if (!num_rows || (num_reqs > 0 && (!prior || !new_tokens))) return DSA_ERR_NULL;
+  if (num_reqs < 0 || max_rows < 0) return DSA_ERR_SHAPE;
+  long long total = 0;
+  for (int q = 0; q < num_reqs; ++q) {
+    if (prior[q] < 0 || new_tokens[q] < 0) return DSA_ERR_SHAPE;
+    if ((long long)prior[q] + new_tokens[q] > INT32_MAX) return DSA_ERR_SHAPE;
+    total += new_tokens[q];
+  }
+  if (total > max_rows) return DSA_ERR_SHAPE;
+  if (total > 0 && (!row_req || !row_len)) return DSA_ERR_NULL;
+  int r = 0;
+  for (int q = 0; q < num_reqs; ++q)
+    for (int i = 0; i < new_tokens[q]; ++i, ++r) {
+      row_req[r] = q;
+      row_len[r] = prior[q] + i + 1;
+    }
+  *num_rows = r;
+  return DSA_OK;
+}
+
+int dsa_plan_blocks(int rows, const int32_t* row_req, int max_rows_per_block, int max_blocks,
+                    int32_t* blocks, int* num_blocks) {
+  if (!num_blocks || (rows > 0 && (!row_req || !blocks))) return DSA_ERR_NULL;
+  if (rows < 0 || max_rows_per_block < 1 || max_blocks < 0) return DSA_ERR_SHAPE;
+  int nb = 0;
+  for (int r = 0; r < rows;) {
+    int e = r + 1;
+    while (e < rows && row_req[e] == row_req[r] && e - r < max_rows_per_block) ++e;
+    if (nb >= max_blocks) return DSA_ERR_SHAPE;
+    blocks[2 * nb] = r;
+    blocks[2 * nb + 1] = e - r;
+    ++nb;
+    r = e;
+  }
+  *num_blocks = nb;
+  return DSA_OK;
+}
+
+int dsa_score_width(int rows, const int32_t* row_len, int* width) {
+  if (!width || (rows > 0 && !row_len)) return DSA_ERR_NULL;
+  if (rows < 0) return DSA_ERR_SHAPE;
+  int mx = 0;
+  for (int r = 0; r < rows; ++r) {
+    if (row_len[r] < 0) return DSA_ERR_SHAPE;
+    if (row_len[r] > mx) mx = row_len[r];
+  }
+  if (mx > INT32_MAX - 63) return DSA_ERR_SHAPE;
+  const int w = ((mx + 63) / 64) * 64;
+  *width = w < 64 ? 64 : w;
+  return DSA_OK;
+}
+
+int dsa_indexer_scores(const void* q_idx, const float* w, const void* k_idx_cache,
+                       const int32_t* block_table, const int32_t* row_req, const int32_t* row_len,
+                       const int32_t* blocks, int num_blocks, float* scores, int rows, int width,
+                       int num_heads, int head_dim, int page_size, int max_pages, dsa_dtype dtype,
+                       void* stream) {
+  if (!q_idx || !w || !k_idx_cache || !block_table || !row_req || !row_len || !scores)
+    return DSA_ERR_NULL;
+  if (rows < 0 || width < 1 || (width & 3) != 0 || max_pages < 1) return DSA_ERR_SHAPE;
+  const int ps = pow2_shift(page_size);
+  if (ps < 0) return DSA_ERR_SHAPE;
+  if (blocks) {
+    if (num_blocks < 1 || num_blocks > rows) return DSA_ERR_SHAPE;
+  } else {
+    num_blocks = rows;
+  }
+  if (dtype == DSA_BF16) {
+    if (!((head_dim == 128 || head_dim == 64) && (num_heads == 32 || num_heads == 64)))
+      return DSA_ERR_UNSUPPORTED;
+  } else if (dtype == DSA_F32) {
+    if (!((head_dim == 32 || head_dim == 64 || head_dim == 128) && num_heads >= 1 &&
+          num_heads <= 64))
+      return DSA_ERR_UNSUPPORTED;
+  } else {
+    return DSA_ERR_UNSUPPORTED;
+  }
+  if (!aligned(q_idx, 16) || !aligned(k_idx_cache, 16) || !aligned(scores, 16) || !aligned(w, 4) ||
+      !aligned(block_table, 4) || !aligned(row_req, 4) || !aligned(row_len, 4) ||
+      (blocks && !aligned(blocks, 4)))
+    return DSA_ERR_ALIGN;
+  if (rows == 0) return DSA_OK;
+  const int chunk = dtype == DSA_BF16 ? dsa::indexer_chunk_keys(num_blocks, width) : 256;
+  if ((long long)num_blocks * ((width + chunk - 1) / chunk) > INT32_MAX) return DSA_ERR_SHAPE;
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (dtype == DSA_BF16)
+    return launch_status(dsa::launch_indexer_bf16(q_idx, w, k_idx_cache, block_table, row_req,
+                                                  row_len, blocks, num_blocks, scores, width,
+                                                  num_heads, head_dim, ps, max_pages, st));
+  return launch_status(dsa::launch_indexer_f32(
+      static_cast<const float*>(q_idx), w, static_cast<const float*>(k_idx_cache), block_table,
+      row_req, row_len, blocks, num_blocks, scores, width, num_heads, head_dim, ps, max_pages, st));
+}
+
+int dsa_topk(const float* scores, const int32_t* row_len, int rows, int width, int k,
+             int32_t* idx, void* stream) {
+  if (!scores || !row_len || !idx) return DSA_ERR_NULL;
+  if (rows < 0 || width < 1 || (width & 3) != 0 || k < 1 || k > width) return DSA_ERR_SHAPE;
+  if (!aligned(scores, 16) || !aligned(row_len, 4) || !aligned(idx, 4)) return DSA_ERR_ALIGN;
+  if (rows == 0) return DSA_OK;
+  return launch_status(
+      dsa::launch_topk(scores, row_len, rows, width, k, idx, static_cast<hipStream_t>(stream)));
+}
+
+int dsa_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
+                    const int32_t* block_table, const int32_t* row_req, const int32_t* idx,
+                    int rows, int num_q_heads, int num_kv_heads, int head_dim, int k,
+                    int page_size, int max_pages, float scale, int num_splits, float* part_o,
+                    float* part_lse, dsa_dtype dtype, void* stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !row_req || !idx || !part_o || !part_lse)
+    return DSA_ERR_NULL;
+  if (rows < 0 || num_q_heads < 1 || num_kv_heads < 1 || k < 1 || max_pages < 1 ||
+      num_splits < 1 || num_splits > k || !isfinite(scale))
+    return DSA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return DSA_ERR_SHAPE;
+  const int ps = pow2_shift(page_size);
+  if (ps < 0) return DSA_ERR_SHAPE;
+  const int G = num_q_heads / num_kv_heads;
+  if (!(head_dim == 64 || head_dim == 128) || !(G == 1 || G == 2 || G == 4 || G == 8 || G == 16))
+    return DSA_ERR_UNSUPPORTED;
+  if (dtype != DSA_BF16 && dtype != DSA_F32) return DSA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(part_o, 16) ||
+      !aligned(part_lse, 4) || !aligned(block_table, 4) || !aligned(row_req, 4) ||
+      !aligned(idx, 4))
+    return DSA_ERR_ALIGN;
+  if (rows == 0) return DSA_OK;
+  if ((long long)rows * num_splits * num_kv_heads > INT32_MAX) return DSA_ERR_SHAPE;
+  return launch_status(dsa::launch_sparse_attn(
+      q, k_cache, v_cache, block_table, row_req, idx, rows, num_q_heads, num_kv_heads, head_dim,
+      k, ps, max_pages, scale, num_splits, part_o, part_lse, dtype == DSA_BF16,
+      static_cast<hipStream_t>(stream)));
+}
+
+int dsa_merge(const float* part_o, const float* part_lse, int rows, int num_q_heads, int head_dim,
+              int num_splits, void* out, float* out_lse, dsa_dtype out_dtype, void* stream) {
+  if (!part_o || !part_lse || !out) return DSA_ERR_NULL;
+  if (rows < 0 || num_q_heads < 1 || head_dim < 1 || head_dim > 256 || num_splits < 1)
+    return DSA_ERR_SHAPE;
+  if (out_dtype != DSA_BF16 && out_dtype != DSA_F32) return DSA_ERR_UNSUPPORTED;
+  if (!aligned(part_o, 16) || !aligned(out, 16) || !aligned(part_lse, 4) ||
+      (out_lse && !aligned(out_lse, 4)))
+    return DSA_ERR_ALIGN;
+  if (rows == 0) return DSA_OK;
+  if ((long long)rows * num_q_heads > INT32_MAX - 4) return DSA_ERR_SHAPE;
+  return launch_status(dsa::launch_merge(part_o, part_lse, rows, num_q_heads, head_dim,
+                                         num_splits, out, out_lse, out_dtype == DSA_BF16,
+                                         static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

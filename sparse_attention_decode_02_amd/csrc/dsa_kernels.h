@@ -1,0 +1,49 @@
+// Internal launcher interface between the C ABI (dsa_api.cpp) and the HIP
+// kernels. Arguments are validated by the caller; every launcher enqueues on
+// `stream` and returns hipGetLastError() of its launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dsa {
+
+// Keys a workgroup of the indexer covers for one row: a multiple of 128.
+int indexer_chunk_keys(int num_blocks, int width);
+
+hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kcache,
+                               const int32_t* bt, const int32_t* row_req, const int32_t* row_len,
+                               const int32_t* blocks, int num_blocks, float* scores, int width,
+                               int num_heads, int head_dim, int page_shift, int max_pages,
+                               hipStream_t stream);
+
+hipError_t launch_indexer_f32(const float* q_idx, const float* w, const float* kcache,
+                              const int32_t* bt, const int32_t* row_req, const int32_t* row_len,
+                              const int32_t* blocks, int num_blocks, float* scores, int width,
+                              int num_heads, int head_dim, int page_shift, int max_pages,
+                              hipStream_t stream);
+
+hipError_t launch_topk(const float* scores, const int32_t* row_len, int rows, int width, int k,
+                       int32_t* idx, hipStream_t stream);
+
+hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, const int32_t* bt,
+                              const int32_t* row_req, const int32_t* idx, int rows, int hq,
+                              int hkv, int d, int k, int page_shift, int max_pages, float scale,
+                              int num_splits, float* part_o, float* part_lse, bool bf16,
+                              hipStream_t stream);
+
+hipError_t launch_merge(const float* part_o, const float* part_lse, int rows, int hq, int d,
+                        int num_splits, void* out, float* out_lse, bool out_bf16,
+                        hipStream_t stream);
+
+// Workgroup id -> work item such that the items each XCD runs form one
+// contiguous range. Workgroups are dispatched round-robin over the 8 XCDs
+// (workgroup i runs on XCD i % 8); item ranges that share data (the key
+// chunks of one row, the rows of one request) then share that XCD's L2.
+__device__ __forceinline__ int xcd_contiguous(int wg, int n) {
+  const int q = n >> 3, r = n & 7;
+  const int x = wg & 7, j = wg >> 3;
+  return (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
+}
+
+}  // namespace dsa

@@ -1,0 +1,266 @@
+// Length-bounded exact top-k (Megatron-LM pull request 7211: commit "Replace
+// the CuTe decode kernels with two Triton kernels" reads each row only up to
+// its length; commit "When a step's context bound reaches 64K keys ..." keeps
+// the result the exact top k; commit "Replace the Triton radix selector with
+// torch.topk ..." ranks valid -inf scores ahead of padding).
+//
+// Row r with L = row_len[r] > k: select the k positions of [0, L) with the
+// largest scores, ties to the lower position, and write them in ascending
+// order. L <= k: every position, then -1.
+//
+// One workgroup of 1024 threads per row; a thread owns 32 consecutive
+// positions of each 32768-position chunk, held in registers as order-
+// preserving 32-bit keys (-0.0 canonicalized to +0.0). The threshold key is
+// found by radix select on those keys:
+//   * a min/max reduction skips the bits every key shares, so the first
+//     12-bit digit falls where the row's values actually differ (scores of a
+//     row usually share sign and leading exponent bits, which would otherwise
+//     pile every key into one or two bins);
+//   * each pass histograms the next <= 12 bits of the keys still tied with
+//     the threshold prefix (LDS atomics) and a block scan over the bins, from
+//     the top, picks the digit holding the k-th largest;
+//   * it stops when the bits run out or every key still tied is needed.
+// The emit pass is an ordered compaction: each thread counts its keys above
+// the threshold prefix and equal to it, one block-wide exclusive scan gives
+// every thread its output offset, and keys equal to the prefix are taken in
+// position order until the remaining need is met -- which is exactly
+// "ties to the lower position". Rows longer than 32768 positions re-read
+// their chunks from cache on every pass.
+
+#include "dsa_kernels.h"
+
+namespace dsa {
+
+constexpr int kTopkThreads = 1024;
+constexpr int kTopkWaves = kTopkThreads / 64;
+constexpr int kVPT = 32;                        // positions per thread per chunk
+constexpr int kChunk = kTopkThreads * kVPT;     // 32768
+constexpr int kDigitBits = 12;
+constexpr int kBins = 1 << kDigitBits;
+
+__device__ __forceinline__ uint32_t order_key(float f) {
+  uint32_t u = __float_as_uint(f);
+  if (u == 0x80000000u) u = 0u;  // -0.0 ranks as +0.0
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ uint32_t high_bits(uint32_t key, int shift) {
+  return shift >= 32 ? 0u : (key >> shift);
+}
+
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
+  return v;
+}
+
+// Exclusive prefix sum over the block in thread order; *total gets the sum.
+__device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* sh,
+                                                         uint32_t* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  uint32_t incl = v;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t n = (uint32_t)__shfl_up((int)incl, o);
+    if (lane >= o) incl += n;
+  }
+  if (lane == 63) sh[wave] = incl;
+  __syncthreads();
+  uint32_t base = 0, tot = 0;
+#pragma unroll
+  for (int i = 0; i < kTopkWaves; ++i) {
+    const uint32_t x = sh[i];
+    base += (i < wave) ? x : 0u;
+    tot += x;
+  }
+  __syncthreads();
+  *total = tot;
+  return base + incl - v;
+}
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores,
+                                                           const int32_t* __restrict__ row_len,
+                                                           int width, int k,
+                                                           int32_t* __restrict__ idx) {
+  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t red[2 * kTopkWaves];
+  __shared__ uint32_t pick[3];
+
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int L = row_len[r];
+  int32_t* out = idx + (size_t)r * k;
+  if (L <= k) {
+    for (int i = tid; i < k; i += kTopkThreads) out[i] = i < L ? i : -1;
+    return;
+  }
+  const float* row = scores + (size_t)r * width;
+  const int nchunks = (L + kChunk - 1) / kChunk;
+  uint32_t key[kVPT];
+
+  auto load_chunk = [&](int c) {
+    const int base = c * kChunk + tid * kVPT;
+#pragma unroll
+    for (int j = 0; j < kVPT; j += 4) {
+      const int p = base + j;
+      if (p + 3 < L) {
+        const float4 v = *reinterpret_cast<const float4*>(row + p);
+        key[j] = order_key(v.x);
+        key[j + 1] = order_key(v.y);
+        key[j + 2] = order_key(v.z);
+        key[j + 3] = order_key(v.w);
+      } else {
+#pragma unroll
+        for (int e = 0; e < 4; ++e) key[j + e] = (p + e < L) ? order_key(row[p + e]) : 0u;
+      }
+    }
+  };
+  const bool resident = (nchunks == 1);
+  if (resident) load_chunk(0);
+
+  // ---- min / max over the row --------------------------------------------
+  uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+  for (int c = 0; c < nchunks; ++c) {
+    if (!resident) load_chunk(c);
+    const int base = c * kChunk + tid * kVPT;
+#pragma unroll
+    for (int j = 0; j < kVPT; ++j) {
+      if (base + j < L) {
+        mx = max(mx, key[j]);
+        mn = min(mn, key[j]);
+      }
+    }
+  }
+  mx = wave_max_u32(mx);
+  mn = wave_min_u32(mn);
+  if (lane == 0) {
+    red[wave] = mx;
+    red[kTopkWaves + wave] = mn;
+  }
+  __syncthreads();
+  mx = 0u;
+  mn = 0xFFFFFFFFu;
+#pragma unroll
+  for (int i = 0; i < kTopkWaves; ++i) {
+    mx = max(mx, red[i]);
+    mn = min(mn, red[kTopkWaves + i]);
+  }
+  __syncthreads();  // `red` is reused by the scans below
+
+  // ---- radix select of the threshold prefix --------------------------------
+  // Candidates are the keys whose bits above `shift` equal `prefix`; `need`
+  // of them still have to be taken, and every key above the prefix is taken.
+  int shift;
+  uint32_t prefix;
+  uint32_t need = (uint32_t)k;
+  if (mx == mn) {
+    shift = 0;
+    prefix = mx;
+  } else {
+    shift = 32 - __clz(mx ^ mn);
+    prefix = high_bits(mx, shift);
+  }
+  while (shift > 0) {
+    const int nb = min(kDigitBits, shift);
+    const int ns = shift - nb;
+    const int nbins = 1 << nb;
+    const uint32_t dmask = (uint32_t)nbins - 1u;
+    for (int i = tid; i < nbins; i += kTopkThreads) hist[i] = 0u;
+    __syncthreads();
+    for (int c = 0; c < nchunks; ++c) {
+      if (!resident) load_chunk(c);
+      const int base = c * kChunk + tid * kVPT;
+#pragma unroll
+      for (int j = 0; j < kVPT; ++j) {
+        if (base + j < L && high_bits(key[j], shift) == prefix)
+          atomicAdd(&hist[(key[j] >> ns) & dmask], 1u);
+      }
+    }
+    __syncthreads();
+    // Bins in descending digit order; thread t owns ranks [t*bpt, t*bpt+bpt).
+    const int bpt = (nbins + kTopkThreads - 1) / kTopkThreads;
+    uint32_t local = 0;
+    for (int i = 0; i < bpt; ++i) {
+      const int rank = tid * bpt + i;
+      if (rank < nbins) local += hist[nbins - 1 - rank];
+    }
+    uint32_t total;
+    const uint32_t before = block_exclusive_scan(local, red, &total);
+    if (before < need && need <= before + local) {
+      uint32_t run = before;
+      for (int i = 0; i < bpt; ++i) {
+        const int rank = tid * bpt + i;
+        if (rank >= nbins) break;
+        const uint32_t hb = hist[nbins - 1 - rank];
+        if (run + hb >= need) {
+          pick[0] = (uint32_t)(nbins - 1 - rank);
+          pick[1] = run;
+          pick[2] = hb;
+          break;
+        }
+        run += hb;
+      }
+    }
+    __syncthreads();
+    const uint32_t digit = pick[0], above = pick[1], cand = pick[2];
+    __syncthreads();
+    prefix = (prefix << nb) | digit;
+    shift = ns;
+    need -= above;
+    if (cand == need) break;
+  }
+
+  // ---- ordered emit ---------------------------------------------------------
+  uint32_t gt_run = 0, eq_run = 0;
+  for (int c = 0; c < nchunks; ++c) {
+    if (!resident) load_chunk(c);
+    const int base = c * kChunk + tid * kVPT;
+    uint32_t ngt = 0, neq = 0;
+#pragma unroll
+    for (int j = 0; j < kVPT; ++j) {
+      if (base + j < L) {
+        const uint32_t hb = high_bits(key[j], shift);
+        ngt += hb > prefix;
+        neq += hb == prefix;
+      }
+    }
+    uint32_t total;
+    const uint32_t excl = block_exclusive_scan((ngt << 16) | neq, red, &total);
+    uint32_t g = gt_run + (excl >> 16);
+    uint32_t e = eq_run + (excl & 0xFFFFu);
+#pragma unroll
+    for (int j = 0; j < kVPT; ++j) {
+      if (base + j < L) {
+        const uint32_t hb = high_bits(key[j], shift);
+        // Every slot written is < k by construction; the bound keeps a
+        // broken invariant from ever turning into an out-of-row store.
+        if (hb > prefix) {
+          const uint32_t slot = g + min(e, need);
+          if (slot < (uint32_t)k) out[slot] = base + j;
+          ++g;
+        } else if (hb == prefix) {
+          if (e < need && g + e < (uint32_t)k) out[g + e] = base + j;
+          ++e;
+        }
+      }
+    }
+    gt_run += total >> 16;
+    eq_run += total & 0xFFFFu;
+  }
+}
+
+hipError_t launch_topk(const float* scores, const int32_t* row_len, int rows, int width, int k,
+                       int32_t* idx, hipStream_t stream) {
+  hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kTopkThreads), 0, stream, scores, row_len,
+                     width, k, idx);
+  return hipGetLastError();
+}
+
+}  // namespace dsa

@@ -1,0 +1,198 @@
+"""Python binding of libdsa.so: argument marshalling only.
+
+Each function takes torch tensors, checks that they are contiguous, on the
+GPU and of the expected dtype, and passes their data pointers, the sizes and
+torch's current HIP stream to the C entry point of the same name; every step
+of the computation runs in the library's HIP kernels. A negative status raises
+``DsaError``. Importing this module loads the library and raises ImportError
+when it has not been built; there is no fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libdsa.so")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(
+        f"{LIB_PATH} is missing: build it with `python -m sparse_attention_decode_02_amd.build`")
+
+_lib = ctypes.CDLL(LIB_PATH)
+
+_P = ctypes.c_void_p
+_I = ctypes.c_int
+_F = ctypes.c_float
+_IP = ctypes.POINTER(ctypes.c_int32)
+
+F32, BF16 = 0, 1
+
+_SIGS = {
+    "dsa_status_string": (ctypes.c_char_p, [_I]),
+    "dsa_abi_version": (_I, []),
+    "dsa_plan_rows": (_I, [_I, _P, _P, _I, _P, _P, ctypes.POINTER(_I)]),
+    "dsa_plan_blocks": (_I, [_I, _P, _I, _I, _P, ctypes.POINTER(_I)]),
+    "dsa_score_width": (_I, [_I, _P, ctypes.POINTER(_I)]),
+    "dsa_indexer_scores": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "dsa_topk": (_I, [_P, _P, _I, _I, _I, _P, _P]),
+    "dsa_sparse_attn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I, _P]),
+    "dsa_merge": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _P]),
+}
+for _name, (_res, _args) in _SIGS.items():
+    _fn = getattr(_lib, _name)
+    _fn.restype = _res
+    _fn.argtypes = _args
+
+EXPORTS = tuple(_SIGS)
+
+
+class DsaError(RuntimeError):
+    def __init__(self, fn, status):
+        super().__init__(f"{fn} failed: {status} ({status_string(status)})")
+        self.status = status
+
+
+def status_string(status: int) -> str:
+    return _lib.dsa_status_string(int(status)).decode()
+
+
+def abi_version() -> int:
+    return _lib.dsa_abi_version()
+
+
+def _check(fn, status):
+    if status != 0:
+        raise DsaError(fn, status)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return F32
+    raise TypeError(f"unsupported dtype {t.dtype}")
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be on the GPU")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+# --------------------------------------------------------------------------
+# Row plan (host)
+# --------------------------------------------------------------------------
+
+
+def _host_i32(x):
+    import numpy as np
+    return np.ascontiguousarray(np.asarray(x, dtype=np.int32))
+
+
+def plan_rows(prior, new):
+    """(row_req, row_len) int32 NumPy arrays from dsa_plan_rows."""
+    import numpy as np
+    p, n = _host_i32(prior), _host_i32(new)
+    if p.shape != n.shape:
+        raise ValueError("prior and new differ in length")
+    total = int(n.astype(np.int64).sum()) if n.size else 0
+    req = np.zeros(max(total, 1), np.int32)
+    ln = np.zeros(max(total, 1), np.int32)
+    nr = _I(0)
+    _check("dsa_plan_rows", _lib.dsa_plan_rows(len(p), p.ctypes.data, n.ctypes.data, total,
+                                               req.ctypes.data, ln.ctypes.data, ctypes.byref(nr)))
+    return req[: nr.value].copy(), ln[: nr.value].copy()
+
+
+def plan_blocks(row_req, max_rows_per_block):
+    """Score blocks int32 [num_blocks][2] (first_row, n_rows) from dsa_plan_blocks."""
+    import numpy as np
+    rq = _host_i32(row_req)
+    blocks = np.zeros((max(len(rq), 1), 2), np.int32)
+    nb = _I(0)
+    _check("dsa_plan_blocks", _lib.dsa_plan_blocks(len(rq), rq.ctypes.data, int(max_rows_per_block),
+                                                   len(blocks), blocks.ctypes.data, ctypes.byref(nb)))
+    return blocks[: nb.value].copy()
+
+
+def score_width(row_len) -> int:
+    ln = _host_i32(row_len)
+    w = _I(0)
+    _check("dsa_score_width", _lib.dsa_score_width(len(ln), ln.ctypes.data, ctypes.byref(w)))
+    return w.value
+
+
+# --------------------------------------------------------------------------
+# Kernels
+# --------------------------------------------------------------------------
+
+
+def indexer_scores(q_idx, w, k_idx_cache, block_table, row_req, row_len, scores, page_size,
+                   blocks=None, stream=None):
+    """dsa_indexer_scores: writes scores[r][:row_len[r]] in place."""
+    rows, heads, dim = q_idx.shape
+    dt = _dtype_code(q_idx)
+    if k_idx_cache.dtype != q_idx.dtype:
+        raise TypeError("q_idx and k_idx_cache dtypes differ")
+    nb = 0 if blocks is None else int(blocks.shape[0])
+    _check("dsa_indexer_scores", _lib.dsa_indexer_scores(
+        _dev(q_idx, "q_idx"), _dev(w, "w", torch.float32), _dev(k_idx_cache, "k_idx_cache"),
+        _dev(block_table, "block_table", torch.int32), _dev(row_req, "row_req", torch.int32),
+        _dev(row_len, "row_len", torch.int32),
+        None if blocks is None else _dev(blocks, "blocks", torch.int32), nb,
+        _dev(scores, "scores", torch.float32), rows, int(scores.shape[1]), heads, dim,
+        int(page_size), int(block_table.shape[1]), dt, _stream(stream)))
+    return scores
+
+
+def topk(scores, row_len, k, idx, stream=None):
+    """dsa_topk: writes idx [rows][k] in place."""
+    rows, width = scores.shape
+    _check("dsa_topk", _lib.dsa_topk(
+        _dev(scores, "scores", torch.float32), _dev(row_len, "row_len", torch.int32), rows, width,
+        int(k), _dev(idx, "idx", torch.int32), _stream(stream)))
+    return idx
+
+
+def sparse_attn(q, k_cache, v_cache, block_table, row_req, idx, page_size, scale, num_splits,
+                part_o, part_lse, stream=None):
+    """dsa_sparse_attn: writes part_o [rows][Hq][S][d] and part_lse [rows][Hq][S]."""
+    rows, hq, d = q.shape
+    hkv = k_cache.shape[2]
+    dt = _dtype_code(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
+        raise TypeError("q, k_cache and v_cache dtypes differ")
+    _check("dsa_sparse_attn", _lib.dsa_sparse_attn(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_table, "block_table", torch.int32), _dev(row_req, "row_req", torch.int32),
+        _dev(idx, "idx", torch.int32), rows, hq, hkv, d, int(idx.shape[1]), int(page_size),
+        int(block_table.shape[1]), float(scale), int(num_splits),
+        _dev(part_o, "part_o", torch.float32), _dev(part_lse, "part_lse", torch.float32), dt,
+        _stream(stream)))
+    return part_o, part_lse
+
+
+def merge(part_o, part_lse, out, out_lse=None, stream=None):
+    """dsa_merge: writes out [rows][Hq][d] (and out_lse [rows][Hq] if given)."""
+    rows, hq, S, d = part_o.shape
+    _check("dsa_merge", _lib.dsa_merge(
+        _dev(part_o, "part_o", torch.float32), _dev(part_lse, "part_lse", torch.float32), rows, hq,
+        d, S, _dev(out, "out"), None if out_lse is None else _dev(out_lse, "out_lse", torch.float32),
+        _dtype_code(out), _stream(stream)))
+    return out, out_lse

@@ -1,0 +1,78 @@
+"""One paged DSA step on the GPU: the row plan, the buffers between the stages,
+and the four library calls in order on one stream.
+
+torch supplies only the device memory and the stream; the row plan comes
+from the library's host entry points and every stage runs in its kernels.
+The metadata is copied to the device once, at construction, so ``run`` issues
+the four launches with no host synchronization.
+"""
+
+from __future__ import annotations
+
+import torch
+
+from . import lib
+
+
+def default_splits(rows: int, hkv: int, k: int) -> int:
+    """Splits of the k slots per (row, KV group): enough waves to cover the
+    chip (about 4096), and at least 64 slots per split."""
+    s = 1
+    while rows * hkv * s < 4096 and (2 * s) * 64 <= k:
+        s *= 2
+    return s
+
+
+class DsaStep:
+    """Buffers and launches for one step of ``inp`` (a StepInputs on a CUDA
+    device). ``block_rows`` > 1 groups consecutive rows of a request into
+    score blocks for the indexer."""
+
+    def __init__(self, inp, num_splits: int | None = None, block_rows: int = 1):
+        wl = inp.wl
+        dev = inp.q.device
+        self.inp = inp
+        self.wl = wl
+        req, ln = lib.plan_rows(wl.prior, wl.new)
+        self.row_req_host, self.row_len_host = req, ln
+        self.rows = len(req)
+        self.width = lib.score_width(ln)
+        self.row_req = torch.from_numpy(req).to(dev)
+        self.row_len = torch.from_numpy(ln).to(dev)
+        self.blocks = None
+        if block_rows > 1:
+            self.blocks = torch.from_numpy(lib.plan_blocks(req, block_rows)).to(dev)
+        self.num_splits = num_splits or default_splits(self.rows, wl.hkv, wl.topk)
+        self.scores = torch.empty(self.rows, self.width, dtype=torch.float32, device=dev)
+        self.idx = torch.empty(self.rows, wl.topk, dtype=torch.int32, device=dev)
+        self.part_o = torch.empty(self.rows, wl.hq, self.num_splits, wl.d, dtype=torch.float32,
+                                  device=dev)
+        self.part_lse = torch.empty(self.rows, wl.hq, self.num_splits, dtype=torch.float32,
+                                    device=dev)
+        self.out = torch.empty(self.rows, wl.hq, wl.d, dtype=inp.q.dtype, device=dev)
+        self.out_lse = torch.empty(self.rows, wl.hq, dtype=torch.float32, device=dev)
+
+    # The four stages, each one library call.
+    def indexer(self, stream=None):
+        i = self.inp
+        lib.indexer_scores(i.qI, i.w, i.kI_cache, i.block_table, self.row_req, self.row_len,
+                           self.scores, self.wl.page, blocks=self.blocks, stream=stream)
+
+    def topk(self, stream=None):
+        lib.topk(self.scores, self.row_len, self.wl.topk, self.idx, stream=stream)
+
+    def attention(self, stream=None):
+        i = self.inp
+        lib.sparse_attn(i.q, i.k_cache, i.v_cache, i.block_table, self.row_req, self.idx,
+                        self.wl.page, self.wl.attn_scale, self.num_splits, self.part_o,
+                        self.part_lse, stream=stream)
+
+    def merge(self, stream=None):
+        lib.merge(self.part_o, self.part_lse, self.out, self.out_lse, stream=stream)
+
+    def run(self, stream=None):
+        self.indexer(stream)
+        self.topk(stream)
+        self.attention(stream)
+        self.merge(stream)
+        return self.out

@@ -1,0 +1,190 @@
+"""CPU tests of the C ABI: the library loads without a GPU, exports every
+symbol include/dsa.h declares, plans rows exactly as the oracle does, and
+rejects every invalid host argument with its status code before any launch.
+No test here enqueues GPU work: every kernel entry point is called only with
+arguments it must reject (or with zero rows, which returns before launching).
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import dsa_oracle as O
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+lib = pytest.importorskip("sparse_attention_decode_02_amd.lib",
+                          reason="libdsa.so not built (python -m sparse_attention_decode_02_amd.build)")
+
+OK, NULL, SHAPE, ALIGN, UNSUP = 0, -1, -2, -3, -4
+
+
+def test_exports_every_declared_symbol():
+    hdr = open(os.path.join(ROOT, "include", "dsa.h")).read()
+    declared = set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(dsa_\w+)\(", hdr, re.M))
+    assert {"dsa_indexer_scores", "dsa_topk", "dsa_sparse_attn", "dsa_merge"} <= declared
+    raw = ctypes.CDLL(lib.LIB_PATH)
+    for name in declared:
+        assert hasattr(raw, name), name
+    assert declared == set(lib.EXPORTS)
+
+
+def test_status_strings():
+    for s in (0, -1, -2, -3, -4, -5, -6):
+        assert lib.status_string(s) and lib.status_string(s) != "unknown status"
+    assert lib.status_string(-99) == "unknown status"
+    assert lib.abi_version() >= 1
+
+
+# --------------------------------------------------------------------------
+# Row plan: bit-exact with the oracle
+# --------------------------------------------------------------------------
+
+
+def test_plan_rows_matches_oracle(golden):
+    g = golden["row_plan"]
+    req, ln = lib.plan_rows(g["prior"], g["new"])
+    assert req.tolist() == g["row_req"] and ln.tolist() == g["row_len"]
+    rng = np.random.default_rng(0)
+    for _ in range(50):
+        n = int(rng.integers(0, 12))
+        prior = rng.integers(0, 10000, n)
+        new = rng.integers(0, 40, n)
+        a = lib.plan_rows(prior, new)
+        b = O.row_plan(prior, new)
+        assert np.array_equal(a[0], b[0]) and np.array_equal(a[1], b[1])
+
+
+def test_plan_blocks_matches_oracle():
+    rng = np.random.default_rng(1)
+    for _ in range(50):
+        req = np.sort(rng.integers(0, 6, int(rng.integers(1, 60)))).astype(np.int32)
+        for m in (1, 2, 5, 16, 128):
+            assert np.array_equal(lib.plan_blocks(req, m), O.score_blocks(req, m))
+
+
+def test_score_width():
+    assert lib.score_width([37, 100]) == 128
+    assert lib.score_width([64]) == 64
+    assert lib.score_width([65]) == 128
+    assert lib.score_width([1]) == 64
+    assert lib.score_width([32768] * 3) == 32768
+
+
+def test_plan_errors():
+    nr = ctypes.c_int(0)
+    p = np.asarray([1, 2], np.int32)
+    n = np.asarray([1, -1], np.int32)
+    out = np.zeros(4, np.int32)
+    assert lib._lib.dsa_plan_rows(2, p.ctypes.data, n.ctypes.data, 4, out.ctypes.data,
+                                  out.ctypes.data, ctypes.byref(nr)) == SHAPE
+    n = np.asarray([3, 3], np.int32)
+    assert lib._lib.dsa_plan_rows(2, p.ctypes.data, n.ctypes.data, 4, out.ctypes.data,
+                                  out.ctypes.data, ctypes.byref(nr)) == SHAPE  # 6 rows > 4
+    assert lib._lib.dsa_plan_rows(2, None, n.ctypes.data, 8, out.ctypes.data, out.ctypes.data,
+                                  ctypes.byref(nr)) == NULL
+    big = np.asarray([2**31 - 1], np.int32)
+    one = np.asarray([1], np.int32)
+    assert lib._lib.dsa_plan_rows(1, big.ctypes.data, one.ctypes.data, 4, out.ctypes.data,
+                                  out.ctypes.data, ctypes.byref(nr)) == SHAPE
+    req = np.asarray([0, 1, 2], np.int32)
+    bl = np.zeros((2, 2), np.int32)
+    assert lib._lib.dsa_plan_blocks(3, req.ctypes.data, 1, 2, bl.ctypes.data, ctypes.byref(nr)) == SHAPE
+    assert lib._lib.dsa_plan_blocks(3, req.ctypes.data, 0, 4, bl.ctypes.data, ctypes.byref(nr)) == SHAPE
+    assert lib._lib.dsa_score_width(1, np.asarray([-1], np.int32).ctypes.data, ctypes.byref(nr)) == SHAPE
+
+
+# --------------------------------------------------------------------------
+# Kernel entry points: argument checks (no launch)
+# --------------------------------------------------------------------------
+
+A = 1 << 20  # a fake 16-byte-aligned device address; never dereferenced
+
+
+def _indexer_args(**kw):
+    a = dict(q_idx=A, w=A, k_idx_cache=A, block_table=A, row_req=A, row_len=A, blocks=None,
+             num_blocks=0, scores=A, rows=4, width=128, num_heads=64, head_dim=128, page_size=64,
+             max_pages=8, dtype=1, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+def _topk_args(**kw):
+    a = dict(scores=A, row_len=A, rows=4, width=128, k=16, idx=A, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+def _attn_args(**kw):
+    a = dict(q=A, k_cache=A, v_cache=A, block_table=A, row_req=A, idx=A, rows=4, hq=64, hkv=8,
+             d=128, k=2048, page_size=64, max_pages=8, scale=0.088, num_splits=8, part_o=A,
+             part_lse=A, dtype=1, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+def _merge_args(**kw):
+    a = dict(part_o=A, part_lse=A, rows=4, hq=64, d=128, num_splits=8, out=A, out_lse=A,
+             dtype=1, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q_idx=None), NULL), (dict(w=None), NULL), (dict(k_idx_cache=None), NULL),
+    (dict(block_table=None), NULL), (dict(row_req=None), NULL), (dict(row_len=None), NULL),
+    (dict(scores=None), NULL),
+    (dict(rows=-1), SHAPE), (dict(width=0), SHAPE), (dict(width=130), SHAPE),
+    (dict(max_pages=0), SHAPE), (dict(page_size=48), SHAPE), (dict(page_size=0), SHAPE),
+    (dict(blocks=A, num_blocks=0), SHAPE), (dict(blocks=A, num_blocks=5), SHAPE),
+    (dict(num_heads=48), UNSUP), (dict(head_dim=96), UNSUP), (dict(dtype=7), UNSUP),
+    (dict(dtype=0, num_heads=65), UNSUP), (dict(dtype=0, head_dim=256), UNSUP),
+    (dict(q_idx=A + 2), ALIGN), (dict(k_idx_cache=A + 8), ALIGN), (dict(scores=A + 4), ALIGN),
+    (dict(w=A + 2), ALIGN), (dict(blocks=A + 2, num_blocks=2), ALIGN),
+    (dict(rows=0), OK),
+])
+def test_indexer_rejects(kw, code):
+    assert lib._lib.dsa_indexer_scores(*_indexer_args(**kw)) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(scores=None), NULL), (dict(row_len=None), NULL), (dict(idx=None), NULL),
+    (dict(rows=-1), SHAPE), (dict(width=0), SHAPE), (dict(width=66), SHAPE), (dict(k=0), SHAPE),
+    (dict(k=129), SHAPE), (dict(scores=A + 4), ALIGN), (dict(idx=A + 1), ALIGN),
+    (dict(rows=0), OK),
+])
+def test_topk_rejects(kw, code):
+    assert lib._lib.dsa_topk(*_topk_args(**kw)) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(k_cache=None), NULL), (dict(v_cache=None), NULL),
+    (dict(block_table=None), NULL), (dict(row_req=None), NULL), (dict(idx=None), NULL),
+    (dict(part_o=None), NULL), (dict(part_lse=None), NULL),
+    (dict(rows=-1), SHAPE), (dict(hq=0), SHAPE), (dict(hkv=0), SHAPE), (dict(hkv=3), SHAPE),
+    (dict(k=0), SHAPE), (dict(max_pages=0), SHAPE), (dict(num_splits=0), SHAPE),
+    (dict(num_splits=2049), SHAPE), (dict(page_size=100), SHAPE),
+    (dict(scale=float("inf")), SHAPE), (dict(scale=float("nan")), SHAPE),
+    (dict(d=96), UNSUP), (dict(hq=24, hkv=8), UNSUP), (dict(hq=64, hkv=2), UNSUP),
+    (dict(dtype=5), UNSUP),
+    (dict(q=A + 2), ALIGN), (dict(k_cache=A + 4), ALIGN), (dict(v_cache=A + 8), ALIGN),
+    (dict(part_o=A + 4), ALIGN), (dict(part_lse=A + 2), ALIGN), (dict(idx=A + 2), ALIGN),
+    (dict(rows=0), OK),
+])
+def test_sparse_attn_rejects(kw, code):
+    args = _attn_args(**kw)
+    assert lib._lib.dsa_sparse_attn(*args) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(part_o=None), NULL), (dict(part_lse=None), NULL), (dict(out=None), NULL),
+    (dict(rows=-1), SHAPE), (dict(hq=0), SHAPE), (dict(d=0), SHAPE), (dict(d=257), SHAPE),
+    (dict(num_splits=0), SHAPE), (dict(dtype=3), UNSUP),
+    (dict(part_o=A + 4), ALIGN), (dict(out=A + 2), ALIGN), (dict(out_lse=A + 2), ALIGN),
+    (dict(part_lse=A + 1), ALIGN), (dict(rows=0), OK),
+])
+def test_merge_rejects(kw, code):
+    assert lib._lib.dsa_merge(*_merge_args(**kw)) == code

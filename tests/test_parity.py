@@ -1,0 +1,252 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Scores and indices must match bit for bit; attention partials and outputs
+within max-abs 2e-2 (bf16 inputs) or 1e-5 (fp32 inputs), the log-sum-exp
+within 1e-3 / 1e-5. Small workloads are checked on every row; the three large
+workloads run at full size in the launch configuration the benchmark times,
+with sampled rows checked against the oracle and every row checked for the
+properties of a correct selection.
+"""
+
+import sys
+
+import numpy as np
+import pytest
+import torch
+
+from dsa_check import CANARY, check_properties, check_row, oracle_row, run_step
+from oracle import dsa_oracle as O
+from sparse_attention_decode_02_amd import inputs as I
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _needs_gpu():
+    assert torch.cuda.is_available(), "GPU tests need a GPU"
+    import sparse_attention_decode_02_amd.lib  # noqa: F401  (raises if the library is missing)
+    yield
+    torch.cuda.empty_cache()
+
+
+def _say(msg):
+    print(msg, flush=True)
+    sys.stdout.flush()
+
+
+def _host_inputs(wl):
+    return I.to_device(I.generate(wl, "cpu"), "cuda")
+
+
+def _check_all(step):
+    errs = [check_row(step, r) for r in range(step.rows)]
+    check_properties(step)
+    return {k: max(e[k] for e in errs) for k in errs[0]}
+
+
+# --------------------------------------------------------------------------
+# Small workloads, every row
+# --------------------------------------------------------------------------
+
+
+@pytest.mark.parametrize("S", [1, 2, 3, 16])
+def test_tiny_every_row(S):
+    _say(f"tiny fp32, splits {S}")
+    step = run_step(_host_inputs(I.tiny()), num_splits=S)
+    e = _check_all(step)
+    _say(f"  max errors {e}")
+
+
+def test_decode_b8_every_row():
+    _say("decode batch 8 x 4096, bf16")
+    step = run_step(_host_inputs(I.decode()))
+    e = _check_all(step)
+    _say(f"  splits {step.num_splits}, max errors {e}")
+
+
+def _small_mixed(seed=7, topk=256):
+    prior = (700, 300, 0, 62, 63, 64, 254, 255, 256, 2999, 5000)
+    new = (37, 5, 1, 1, 1, 1, 1, 1, 1, 1, 1)
+    return I.custom(I.decode(), name="small_mixed", hq=16, hkv=2, topk=topk, prior=prior,
+                    new=new, seed=seed)
+
+
+@pytest.mark.parametrize("block_rows", [1, 8])
+@pytest.mark.parametrize("S", [1, 4])
+def test_small_mixed_every_row(block_rows, S):
+    _say(f"small mixed bf16, block_rows {block_rows}, splits {S}")
+    step = run_step(_host_inputs(_small_mixed()), num_splits=S, block_rows=block_rows)
+    lens = step.row_len_host.tolist()
+    assert {1, 63, 64, 65, 255, 256, 257} <= set(lens)  # around k and the page size
+    e = _check_all(step)
+    _say(f"  max errors {e}")
+
+
+@pytest.mark.parametrize("S", [1, 2, 5, 8, 256])
+def test_split_counts(S):
+    _say(f"splits {S}")
+    wl = _small_mixed(seed=11)
+    step = run_step(_host_inputs(wl), num_splits=S)
+    for r in (0, 36, 40, step.rows - 1):
+        check_row(step, r)
+
+
+VARIANTS = [
+    # dtype, page, hq, hkv, d, hi, di, topk
+    ("bf16", 64, 8, 8, 128, 32, 128, 64),
+    ("bf16", 32, 16, 4, 64, 64, 64, 64),
+    ("bf16", 16, 32, 16, 64, 32, 64, 128),
+    ("bf16", 64, 16, 1, 128, 64, 128, 100),
+    ("bf16", 128, 32, 2, 128, 64, 128, 64),
+    ("f32", 16, 4, 1, 64, 4, 32, 16),
+    ("f32", 8, 8, 4, 128, 64, 128, 40),
+    ("f32", 64, 16, 2, 64, 17, 64, 64),
+    ("f32", 32, 16, 1, 128, 1, 32, 33),
+]
+
+
+@pytest.mark.parametrize("v", VARIANTS, ids=lambda v: "-".join(map(str, v)))
+def test_supported_shapes(v):
+    dt, page, hq, hkv, d, hi, di, topk = v
+    _say(f"shape variant {v}")
+    wl = I.custom(I.tiny(), name="variant", dtype=dt, page=page, hq=hq, hkv=hkv, d=d, hi=hi,
+                  di=di, topk=topk, prior=(3, 150, 700, 40), new=(1, 1, 1, 6), seed=1000 + VARIANTS.index(v))
+    step = run_step(_host_inputs(wl))
+    _check_all(step)
+
+
+# --------------------------------------------------------------------------
+# Edge cases fed straight to the stages
+# --------------------------------------------------------------------------
+
+
+def _topk_case_rows(width, k):
+    rng = np.random.default_rng(5)
+    rows = []
+    rows.append(("all equal", np.full(5000, 7.5, np.float32)))
+    rows.append(("increasing", np.arange(4000, dtype=np.float32)))
+    rows.append(("decreasing", np.arange(4000, 0, -1).astype(np.float32)))
+    sc = rng.integers(-3, 4, 6000).astype(np.float32)
+    sc[rng.integers(0, 6000, 500)] = np.inf
+    sc[rng.integers(0, 6000, 500)] = -np.inf
+    rows.append(("infinities", sc))
+    sc = np.where(rng.random(5000) < 0.5, np.float32(-0.0), np.float32(0.0)).astype(np.float32)
+    sc[rng.integers(0, 5000, 100)] = 1.0
+    rows.append(("signed zeros", sc))
+    rows.append(("all -inf", np.full(3000, -np.inf, np.float32)))
+    rows.append(("empty", np.zeros(0, np.float32)))
+    rows.append(("one", np.asarray([3.0], np.float32)))
+    rows.append(("k-1", rng.standard_normal(k - 1).astype(np.float32)))
+    rows.append(("k", rng.standard_normal(k).astype(np.float32)))
+    rows.append(("k+1", rng.standard_normal(k + 1).astype(np.float32)))
+    rows.append(("two values", np.where(rng.random(9000) < 0.3, 1.0, 2.0).astype(np.float32)))
+    rows.append(("normal", rng.standard_normal(30000).astype(np.float32)))
+    rows.append(("chunked ties", (rng.integers(0, 2000, 40000) / 2).astype(np.float32)))
+    rows.append(("chunked long", (rng.integers(0, 50000, width) / 4).astype(np.float32)))
+    rows.append(("chunked huge range", (rng.standard_normal(70000) * 1e30).astype(np.float32)))
+    rows.append(("denormals", (rng.integers(1, 100, 8000) * np.float32(1e-45)).astype(np.float32)))
+    rows.append(("mixed signs", rng.standard_normal(32768).astype(np.float32) * 1e-3))
+    return rows
+
+
+@pytest.mark.parametrize("k", [1, 16, 2048])
+def test_topk_edges(k):
+    from sparse_attention_decode_02_amd import lib
+    width = 70016
+    cases = _topk_case_rows(width, k)
+    _say(f"top-k edges, k {k}, {len(cases)} rows")
+    scores = np.full((len(cases), width), np.nan, np.float32)
+    lens = np.zeros(len(cases), np.int32)
+    for i, (_, sc) in enumerate(cases):
+        scores[i, : len(sc)] = sc
+        lens[i] = len(sc)
+    s_d = torch.from_numpy(scores).cuda()
+    l_d = torch.from_numpy(lens).cuda()
+    idx = torch.full((len(cases), k), -7, dtype=torch.int32, device="cuda")
+    lib.topk(s_d, l_d, k, idx)
+    got = idx.cpu().numpy()
+    for i, (name, sc) in enumerate(cases):
+        want = O.topk_row(sc, len(sc), k)
+        assert np.array_equal(got[i], want), f"{name}: first diff at {np.flatnonzero(got[i] != want)[:5]}"
+
+
+def test_padding_rows_with_zero_length():
+    """Rows of length 0 (padding in a fixed-size batch): no score written, all
+    slots -1, empty attention (o = 0, lse = -inf), merged output 0."""
+    wl = _small_mixed(seed=3)
+    step = run_step(_host_inputs(wl), num_splits=4)
+    pad = [2, 40, step.rows - 1]
+    step.row_len[pad] = 0
+    step.scores.view(torch.int32).fill_(CANARY)
+    step.run()
+    torch.cuda.synchronize()
+    for r in pad:
+        assert bool((step.scores[r].view(torch.int32) == CANARY).all())
+        assert bool((step.idx[r] == -1).all())
+        assert bool(torch.isneginf(step.part_lse[r]).all())
+        assert bool((step.part_o[r] == 0).all())
+        assert bool((step.out[r].float() == 0).all())
+        assert bool(torch.isneginf(step.out_lse[r]).all())
+    # the other rows are unaffected
+    step.row_len_host = step.row_len.cpu().numpy()
+    for r in (0, 41):
+        check_row(step, r)
+
+
+def test_score_blocks_are_bit_identical():
+    wl = _small_mixed(seed=9)
+    inp = _host_inputs(wl)
+    ref = run_step(inp, block_rows=1).scores.clone()
+    for br in (2, 5, 16, 64):
+        s = run_step(inp, block_rows=br).scores
+        assert torch.equal(s.view(torch.int32), ref.view(torch.int32)), f"block_rows {br}"
+
+
+def test_determinism():
+    inp = _host_inputs(I.decode())
+    a = run_step(inp)
+    outs = [t.clone() for t in (a.scores, a.idx, a.part_o, a.part_lse, a.out, a.out_lse)]
+    b = run_step(inp)
+    for x, y in zip(outs, (b.scores, b.idx, b.part_o, b.part_lse, b.out, b.out_lse)):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+
+
+# --------------------------------------------------------------------------
+# Full-size workloads (the benchmark's launch configuration), sampled rows
+# --------------------------------------------------------------------------
+
+
+def _full(wl, rows_fn):
+    _say(f"{wl.name}: generating on the device")
+    inp = I.generate(wl, "cuda")
+    step = run_step(inp)
+    _say(f"  rows {step.rows}, width {step.width}, splits {step.num_splits}")
+    check_properties(step)
+    rows = rows_fn(step)
+    errs = {}
+    for r in rows:
+        e = check_row(step, r)
+        errs = {k: max(errs.get(k, 0.0), v) for k, v in e.items()}
+        _say(f"  row {r} (L={int(step.row_len_host[r])}) ok")
+    _say(f"  max errors {errs}")
+    del step, inp
+    torch.cuda.empty_cache()
+
+
+def test_headline_full_size():
+    _full(I.headline(), lambda s: [0, 1, 37, s.rows - 1])
+
+
+def test_ragged_full_size():
+    def rows(s):
+        L = s.row_len_host
+        short = [r for r in range(s.rows) if 1 < L[r] < 2048]
+        return sorted({int(np.argmin(L)), int(np.argmax(L)), short[0], 5, 50})
+    _full(I.ragged(), rows)
+
+
+def test_mixed_full_size():
+    def rows(s):
+        L = s.row_len_host
+        return sorted({0, 511, 512, 2047, int(np.argmax(L)), 2050, s.rows - 1})
+    _full(I.mixed(), rows)
