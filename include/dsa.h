@@ -129,9 +129,9 @@ int dsa_score_width(int rows, const int32_t* row_len, int* width);
  *                for one row per block; rows of a block share a request
  *   scores       device [rows][width]                   float32 (output)
  *
- * Supported: bf16 with head_dim in {64, 128} and num_heads in {32, 64};
- * fp32 with head_dim in {32, 64, 128} and 1 <= num_heads <= 64.
- * page_size is a power of two; width is a positive multiple of 4; q_idx,
+ * Supported: bf16 with head_dim in {64, 128}, num_heads in {32, 64} and
+ * page_size >= 16; fp32 with head_dim in {32, 64, 128} and 1 <= num_heads
+ * <= 64. page_size is a power of two; width is a positive multiple of 4; q_idx,
  * k_idx_cache and scores are 16-byte aligned.
  * ------------------------------------------------------------------------ */
 int dsa_indexer_scores(const void* q_idx, const float* w, const void* k_idx_cache,

@@ -113,7 +113,8 @@ int dsa_indexer_scores(const void* q_idx, const float* w, const void* k_idx_cach
     num_blocks = rows;
   }
   if (dtype == DSA_BF16) {
-    if (!((head_dim == 128 || head_dim == 64) && (num_heads == 32 || num_heads == 64)))
+    if (!((head_dim == 128 || head_dim == 64) && (num_heads == 32 || num_heads == 64)) ||
+        page_size < 16)
       return DSA_ERR_UNSUPPORTED;
   } else if (dtype == DSA_F32) {
     if (!((head_dim == 32 || head_dim == 64 || head_dim == 128) && num_heads >= 1 &&

@@ -6,14 +6,13 @@
 //   scores[r][s] = sum_h w[r][h] * max(0, qI[r][h] . kI[req(r)][s]),  s < L_r
 //
 // bf16 path (MFMA): per row the contraction is (heads x dim) . (dim x keys).
-// One wave computes a 32-key tile for all heads with
-// v_mfma_f32_32x32x16_bf16, heads on the M side (32 per head tile) and keys
-// on the N side. A lane owns one key (lane % 32) and one half of its dims
-// (lane / 32), so its B fragments are 64 contiguous bytes per MFMA step of
-// that key's row: the k index of MFMA step kk, lane half hf, element e is
-// dim hf * D/2 + kk * 8 + e, for both operands. After the MFMAs a lane holds
-// 16 heads of its key per head tile; ReLU, the head weight and the head sum
-// run in fp32 registers and one cross-half exchange finishes the key.
+// One wave computes a 16-key tile for all heads with v_mfma_f32_16x16x32_bf16
+// (heads as rows, 16 per head tile; keys as columns). Four lanes share a key
+// and read 64 contiguous bytes of its row per MFMA step; three key tiles
+// rotate through registers so two are in flight while one is on the matrix
+// cores. After the MFMAs a lane holds 4 consecutive heads of its key per head
+// tile; ReLU, the head weight and the head sum run in fp32 registers and two
+// row swaps (v_permlane16_swap, v_permlane32_swap) finish the key.
 // Products of bf16 are exact and the configs' dyadic integers accumulate
 // exactly in fp32, in any order.
 //
@@ -30,23 +29,41 @@
 namespace dsa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kIdxThreads = 256;  // 4 waves
-constexpr int kTileKeys = 32;     // keys per MFMA tile (N of 32x32x16)
+constexpr int kTileKeys = 16;     // keys per MFMA tile (N of 16x16x32)
+constexpr int kKeyBufs = 3;       // key tiles per wave: 2 in flight + 1 on the matrix cores
 
+// max(x, 0) as a signed-integer max of the bits: one VALU op, -0.0 -> +0.0.
+__device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+
+// x summed over the four 16-lane rows of the wave (every lane gets the total).
+__device__ __forceinline__ float sum_rows(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// MFMA layout (v_mfma_f32_16x16x32_bf16): lane l feeds A row l%16 and B
+// column l%16 with k = (l/16)*8 + e, e < 8, and gets D rows (l/16)*4 + i,
+// i < 4, of column l%16. Heads are the rows (16 per head tile), keys the
+// columns. The k index of step kk, lane group g = l/16, element e is dim
+// kk*32 + g*8 + e for both operands, so the four lanes of a key read 64
+// contiguous bytes of its row per step.
 template <int HT, int DI>
-__global__ __launch_bounds__(kIdxThreads, 2) void indexer_mfma_kernel(
+__global__ __launch_bounds__(kIdxThreads, 3) void indexer_mfma_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w,
     const uint16_t* __restrict__ kc, const int32_t* __restrict__ bt,
     const int32_t* __restrict__ row_req, const int32_t* __restrict__ row_len,
     const int32_t* __restrict__ blocks, float* __restrict__ scores, int width, int page_shift,
     int max_pages, int chunk_keys, int chunks, int total) {
-  constexpr int H = HT * 32;
-  constexpr int KS = DI / 16;  // MFMA steps per head tile
-  constexpr int HALF = DI / 2;
-  __shared__ __attribute__((aligned(16))) uint16_t q_lds[H * DI];
-  __shared__ float w_lds[H];
+  constexpr int H = HT * 16;
+  constexpr int KS = DI / 32;  // MFMA steps per head tile
+  constexpr int QST = DI + 8;  // padded LDS row (elements): the 16 rows read together hit distinct banks
+  __shared__ __attribute__((aligned(16))) uint16_t q_lds[H * QST];
+  __shared__ __attribute__((aligned(16))) float w_lds[H];
 
   const int item = xcd_contiguous(blockIdx.x, total);
   const int b = item / chunks;
@@ -58,62 +75,103 @@ __global__ __launch_bounds__(kIdxThreads, 2) void indexer_mfma_kernel(
   }
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int kl = lane & 31, hf = lane >> 5;
+  const int kl = lane & 15, grp = lane >> 4;
   const int page_mask = (1 << page_shift) - 1;
+
+  // Wave-uniform pieces (readfirstlane makes them SGPRs, so the page lookups
+  // below are scalar loads: they wait on the scalar counter and never on the
+  // key loads still in flight).
+  const int wv = __builtin_amdgcn_readfirstlane(wave);
+  constexpr int kStep = 4 * kTileKeys;  // the workgroup's 4 waves interleave tiles
+  constexpr int QV = H * DI / 8 / kIdxThreads;  // uint4 of the query block per thread
+  static_assert(QV * kIdxThreads * 8 == H * DI, "query block must split evenly over the threads");
 
   for (int rr = 0; rr < nrows; ++rr) {
     const int r = first + rr;
     const int L = row_len[r];
     if (chunk0 >= L) continue;  // uniform over the workgroup
     const int req = row_req[r];
-    __syncthreads();
+    const int32_t* btr = bt + (size_t)req * max_pages;
+    const int end = min(L, chunk0 + chunk_keys);
+    float* out = scores + (size_t)r * width;
+
+    // Key fragments of the 16-key tile at `base` (base is wave-uniform). The
+    // tile lies inside one page (page size >= 16), whose number is one scalar
+    // load. Loads are unconditional -- positions past the row read its last
+    // key and are never stored -- so the load counter stays exact and a
+    // prefetch is never waited on early.
+    auto load_tile = [&](int base, bf16x8 (&kf)[KS]) {
+      const int page = btr[min(base, L - 1) >> page_shift];
+      const int s = min(base + kl, L - 1);
+      const size_t krow = ((size_t)page << page_shift) | (size_t)(s & page_mask);
+      const bf16x8* p = reinterpret_cast<const bf16x8*>(kc + krow * DI + grp * 8);
+#pragma unroll
+      for (int kk = 0; kk < KS; ++kk) kf[kk] = p[kk * 4];
+    };
+
+    // Prologue: the first key tiles, then the query block and head weights,
+    // all in flight together; one wait covers them before the query goes to
+    // LDS.
+    const int base0 = chunk0 + wv * kTileKeys;
+    const int ntiles = (end - base0 + kStep - 1) / kStep;  // this wave's tiles (may be <= 0)
+    bf16x8 kbuf[kKeyBufs][KS];
+#pragma unroll
+    for (int i = 0; i < kKeyBufs - 1; ++i) load_tile(base0 + i * kStep, kbuf[i]);
+    __syncthreads();  // the previous row's readers are done with q_lds / w_lds
     {
       const uint4* src = reinterpret_cast<const uint4*>(qI + (size_t)r * H * DI);
-      uint4* dst = reinterpret_cast<uint4*>(q_lds);
-      for (int i = tid; i < H * DI / 8; i += kIdxThreads) dst[i] = src[i];
-      for (int i = tid; i < H; i += kIdxThreads) w_lds[i] = w[(size_t)r * H + i];
+      uint4 qreg[QV];
+#pragma unroll
+      for (int i = 0; i < QV; ++i) qreg[i] = src[tid + i * kIdxThreads];
+      const float wv_ = tid < H ? w[(size_t)r * H + tid] : 0.0f;
+#pragma unroll
+      for (int i = 0; i < QV; ++i) {
+        const int e = tid + i * kIdxThreads;
+        const int h = e / (DI / 8), c = e - h * (DI / 8);
+        *reinterpret_cast<uint4*>(&q_lds[h * QST + c * 8]) = qreg[i];
+      }
+      if (tid < H) w_lds[tid] = wv_;
     }
     __syncthreads();
 
     bf16x8 qf[HT][KS];
-    float wr[HT][16];
+    float4 wr[HT];
 #pragma unroll
     for (int t = 0; t < HT; ++t) {
 #pragma unroll
       for (int kk = 0; kk < KS; ++kk)
-        qf[t][kk] = *reinterpret_cast<const bf16x8*>(&q_lds[(t * 32 + kl) * DI + hf * HALF + kk * 8]);
-#pragma unroll
-      for (int j = 0; j < 16; ++j) wr[t][j] = w_lds[t * 32 + (j >> 2) * 8 + hf * 4 + (j & 3)];
+        qf[t][kk] = *reinterpret_cast<const bf16x8*>(&q_lds[(t * 16 + kl) * QST + kk * 32 + grp * 8]);
+      wr[t] = *reinterpret_cast<const float4*>(&w_lds[t * 16 + grp * 4]);
     }
 
-    const int32_t* btr = bt + (size_t)req * max_pages;
-    const int end = min(L, chunk0 + chunk_keys);
-    float* out = scores + (size_t)r * width;
-    for (int base = chunk0 + wave * kTileKeys; base < end; base += 4 * kTileKeys) {
-      const int s = base + kl;
-      bf16x8 kf[KS];
-      if (s < L) {
-        const int page = btr[s >> page_shift];
-        const size_t krow = ((size_t)page << page_shift) | (size_t)(s & page_mask);
-        const bf16x8* p = reinterpret_cast<const bf16x8*>(kc + krow * DI + hf * HALF);
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) kf[kk] = p[kk];
-      } else {
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) kf[kk] = bf16x8{};
-      }
+    auto score_tile = [&](int base, const bf16x8 (&kf)[KS]) {
       float part = 0.0f;
 #pragma unroll
       for (int t = 0; t < HT; ++t) {
-        f32x16 acc = {};
+        f32x4 acc = {};
 #pragma unroll
         for (int kk = 0; kk < KS; ++kk)
-          acc = __builtin_amdgcn_mfma_f32_32x32x16_bf16(qf[t][kk], kf[kk], acc, 0, 0, 0);
-#pragma unroll
-        for (int j = 0; j < 16; ++j) part += wr[t][j] * fmaxf(acc[j], 0.0f);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[t][kk], kf[kk], acc, 0, 0, 0);
+        part = fmaf(wr[t].x, relu(acc[0]), part);
+        part = fmaf(wr[t].y, relu(acc[1]), part);
+        part = fmaf(wr[t].z, relu(acc[2]), part);
+        part = fmaf(wr[t].w, relu(acc[3]), part);
       }
-      part += __shfl_xor(part, 32);
-      if (hf == 0 && s < L) out[s] = part + 0.0f;
+      part = sum_rows(part);
+      const int s = base + kl;
+      if (grp == 0 && s < L) out[s] = part + 0.0f;
+    };
+
+    // kKeyBufs key-fragment buffers in rotation: while one tile runs on the
+    // matrix cores the next two are in flight. The trip count is fixed and
+    // every load unconditional, so each wait covers exactly the tile in use.
+    for (int it = 0; it < ntiles; it += kKeyBufs) {
+#pragma unroll
+      for (int u = 0; u < kKeyBufs; ++u) {
+        const int cur = base0 + (it + u) * kStep;
+        load_tile(cur + (kKeyBufs - 1) * kStep, kbuf[(u + kKeyBufs - 1) % kKeyBufs]);
+        if (it + u < ntiles) score_tile(cur, kbuf[u]);
+      }
     }
   }
 }
@@ -193,10 +251,10 @@ hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kc
   hipLaunchKernelGGL((indexer_mfma_kernel<HT, DI>), dim3(total), dim3(kIdxThreads), 0, stream, \
                      q, w, k, bt, row_req, row_len, blocks, scores, width, page_shift,         \
                      max_pages, chunk, chunks, total)
-  if (num_heads == 64 && head_dim == 128) DSA_IDX_LAUNCH(2, 128);
-  else if (num_heads == 32 && head_dim == 128) DSA_IDX_LAUNCH(1, 128);
-  else if (num_heads == 64 && head_dim == 64) DSA_IDX_LAUNCH(2, 64);
-  else if (num_heads == 32 && head_dim == 64) DSA_IDX_LAUNCH(1, 64);
+  if (num_heads == 64 && head_dim == 128) DSA_IDX_LAUNCH(4, 128);
+  else if (num_heads == 32 && head_dim == 128) DSA_IDX_LAUNCH(2, 128);
+  else if (num_heads == 64 && head_dim == 64) DSA_IDX_LAUNCH(4, 64);
+  else if (num_heads == 32 && head_dim == 64) DSA_IDX_LAUNCH(2, 64);
   else return hipErrorInvalidValue;
 #undef DSA_IDX_LAUNCH
   return hipGetLastError();

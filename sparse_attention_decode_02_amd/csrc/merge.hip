@@ -5,14 +5,17 @@
 //   M = max_s lse_s,  W = sum_s exp(lse_s - M),
 //   out = sum_s exp(lse_s - M) o_s / W,  out_lse = M + ln W
 //
-// One wave per (row, head); lanes stride over the head dim, so each split's
-// partial row is one coalesced read. bf16 output rounds to nearest even.
+// One wave per (row, head). The split log-sum-exps are read at wave-uniform
+// addresses (scalar loads); each lane owns up to 4 consecutive dims and issues
+// the loads of up to 8 splits before using them. bf16 output rounds to
+// nearest even.
 
 #include "dsa_kernels.h"
 
 namespace dsa {
 
 constexpr int kMergeWaves = 4;
+constexpr int kMergeUnroll = 8;
 
 __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   uint32_t u = __float_as_uint(f);
@@ -21,6 +24,8 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)(u >> 16);
 }
 
+// DPL: dims per lane (d <= 64 * DPL).
+template <int DPL>
 __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(
     const float* __restrict__ part_o, const float* __restrict__ part_lse, int items, int d, int S,
     void* __restrict__ out, float* __restrict__ out_lse, int out_bf16) {
@@ -29,27 +34,43 @@ __global__ __launch_bounds__(64 * kMergeWaves) void merge_kernel(
   if (item >= items) return;
   const float* lse = part_lse + (size_t)item * S;
   float M = -INFINITY;
-  for (int s = lane; s < S; s += 64) M = fmaxf(M, lse[s]);
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) M = fmaxf(M, __shfl_xor(M, o));
+  for (int s = 0; s < S; ++s) M = fmaxf(M, lse[s]);
   const bool any = M != -INFINITY;
-  float W = 0.0f;
-  if (any)
-    for (int s = lane; s < S; s += 64) W += __expf(lse[s] - M);
+  const float Mr = any ? M : 0.0f;  // every weight is exp(-inf - 0) = 0 when nothing is valid
+  const int e0 = lane * DPL;
+  const bool mine = e0 < d;
+  const float* po = part_o + (size_t)item * S * d + e0;
+  float acc[DPL];
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) W += __shfl_xor(W, o);
+  for (int i = 0; i < DPL; ++i) acc[i] = 0.0f;
+  float W = 0.0f;
+  for (int s0 = 0; s0 < S; s0 += kMergeUnroll) {
+    float v[kMergeUnroll][DPL];
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int s = s0 + u;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i)
+        v[u][i] = (s < S && mine && e0 + i < d) ? po[(size_t)s * d + i] : 0.0f;
+    }
+#pragma unroll
+    for (int u = 0; u < kMergeUnroll; ++u) {
+      const int s = s0 + u;
+      const float wgt = s < S ? __expf(lse[s] - Mr) : 0.0f;
+      W += wgt;
+#pragma unroll
+      for (int i = 0; i < DPL; ++i) acc[i] = fmaf(wgt, v[u][i], acc[i]);
+    }
+  }
   const float invW = any ? 1.0f / W : 0.0f;
-  const float* po = part_o + (size_t)item * S * d;
-  for (int e = lane; e < d; e += 64) {
-    float acc = 0.0f;
-    if (any)
-      for (int s = 0; s < S; ++s) {
-        const float ls = lse[s];
-        if (ls != -INFINITY) acc = fmaf(__expf(ls - M), po[(size_t)s * d + e], acc);
-      }
-    const float v = acc * invW;
-    if (out_bf16) static_cast<uint16_t*>(out)[(size_t)item * d + e] = f32_to_bf16_rne(v);
-    else static_cast<float*>(out)[(size_t)item * d + e] = v;
+  if (mine) {
+#pragma unroll
+    for (int i = 0; i < DPL; ++i) {
+      if (e0 + i >= d) break;
+      const float x = acc[i] * invW;
+      if (out_bf16) static_cast<uint16_t*>(out)[(size_t)item * d + e0 + i] = f32_to_bf16_rne(x);
+      else static_cast<float*>(out)[(size_t)item * d + e0 + i] = x;
+    }
   }
   if (out_lse && lane == 0) out_lse[item] = any ? M + __logf(W) : -INFINITY;
 }
@@ -59,8 +80,16 @@ hipError_t launch_merge(const float* part_o, const float* part_lse, int rows, in
                         hipStream_t stream) {
   const int items = rows * hq;
   const int grid = (items + kMergeWaves - 1) / kMergeWaves;
-  hipLaunchKernelGGL(merge_kernel, dim3(grid), dim3(64 * kMergeWaves), 0, stream, part_o,
-                     part_lse, items, d, num_splits, out, out_lse, out_bf16 ? 1 : 0);
+  const int bf = out_bf16 ? 1 : 0;
+  if (d <= 64)
+    hipLaunchKernelGGL(merge_kernel<1>, dim3(grid), dim3(64 * kMergeWaves), 0, stream, part_o,
+                       part_lse, items, d, num_splits, out, out_lse, bf);
+  else if (d <= 128)
+    hipLaunchKernelGGL(merge_kernel<2>, dim3(grid), dim3(64 * kMergeWaves), 0, stream, part_o,
+                       part_lse, items, d, num_splits, out, out_lse, bf);
+  else
+    hipLaunchKernelGGL(merge_kernel<4>, dim3(grid), dim3(64 * kMergeWaves), 0, stream, part_o,
+                       part_lse, items, d, num_splits, out, out_lse, bf);
   return hipGetLastError();
 }
 

@@ -6,20 +6,30 @@
 // through the value reduction).
 //
 // One wave per (row, split, KV group). The split's slots are walked in tiles
-// of 64:
-//   * scores: lane j owns slot j of the tile. It reads the slot's position,
-//     translates it through the block table, loads that key's row for the
-//     group (d elements, contiguous), and dots it with each of the group's G
-//     query heads (queries in LDS, read as broadcasts). bf16 keys use
-//     v_dot2_f32_bf16: the bf16 products are exact and accumulate in fp32.
-//   * online softmax per head in base 2 (the scale folds in log2 e), with one
-//     wave max and one wave sum per head and tile; probabilities go to LDS.
-//   * values: lane owns d/64 consecutive dims of the output; the tile's value
-//     rows are loaded 16 at a time (each a coalesced d-element row read by the
-//     whole wave) and accumulated with fp32 FMAs against the fp32
-//     probabilities.
-// Padding slots (-1) sit at the end of a row's selection; a tile with no
-// valid slot ends the walk, and an empty split writes o = 0, lse = -inf.
+// of 32 tokens:
+//   * addresses: a prologue translates up to 512 selected positions through
+//     the block table into cache row ids in LDS (two dependent round trips
+//     per span, not per tile); tiles past the span's last selected slot are
+//     skipped.
+//   * pipelining: V of tile t is requested before tile t's scores, K of tile
+//     t+1 before tile t's value sums; every load is unconditional (padding
+//     reads cache row 0 with probability 0), so each wait covers exactly the
+//     data in use.
+//   * K: lane t reads the first half of token t's row for the group, lane
+//     t + 32 the second half (two 128-byte runs per 256-byte bf16 row).
+//   * V: for each token j the whole wave reads its row (lane l gets dims
+//     [l*d/64, (l+1)*d/64)), addressed from token j's row id taken from lane j
+//     as a wave-uniform value, so the address arithmetic is scalar.
+//   * scores: each lane dots its half row with the group's G query heads
+//     (LDS broadcasts; v_dot2_f32_bf16 -- exact bf16 products, fp32 sums), and
+//     v_permlane32_swap adds the two halves.
+//   * online softmax in base 2 (the scale folds in log2 e) against a deferred
+//     reference that is raised (one DPP wave max per head, and a rescale)
+//     only when a score overtakes it by more than 2^8; the running sum stays
+//     per lane and is reduced once at the end. Probabilities go to LDS.
+//   * values: fp32 FMAs of the fp32 probabilities into per-lane accumulators.
+// Padding slots (-1) sit at the end of a row's selection; a tile with no valid
+// slot ends the walk, and an empty split writes o = 0, lse = -inf.
 
 #include "dsa_kernels.h"
 
@@ -29,32 +39,70 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr int kTile = 32;   // tokens per tile
+constexpr int kSpan = 512;  // slots whose cache rows are resolved at once
+constexpr float kSlack = 8.0f;  // log2 headroom of the deferred softmax reference
 
-__device__ __forceinline__ float wave_max_f32(float v) {
+// 2^x on the transcendental unit (v_exp_f32); 2^-inf = 0.
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+}
+
+// Max over all 64 lanes, returned wave-uniform.
+__device__ __forceinline__ float wave_max(float v) {
+  v = fmaxf(v, dpp_f32<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f32<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f32<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f32<0x140>(v));  // row_mirror
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return fmaxf(fmaxf(a, b), fmaxf(c, d));
+}
+
+// Sum over all 64 lanes, returned wave-uniform.
+__device__ __forceinline__ float wave_sum(float v) {
+  v += dpp_f32<0xB1>(v);
+  v += dpp_f32<0x4E>(v);
+  v += dpp_f32<0x141>(v);
+  v += dpp_f32<0x140>(v);
+  const float a = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 0));
+  const float b = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 16));
+  const float c = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 32));
+  const float d = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v), 48));
+  return (a + b) + (c + d);
+}
+
+// Max over all 64 lanes of an int, wave-uniform.
+__device__ __forceinline__ int wave_max_i32(int v) {
 #pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
   return v;
 }
 
-__device__ __forceinline__ float wave_sum_f32(float v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+// x[lane] + x[lane ^ 32]
+__device__ __forceinline__ float add_halves(float x) {
+  const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                   false);
+  return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
 }
-
-__device__ __forceinline__ float bf16_lo(uint32_t x) { return __uint_as_float(x << 16); }
-__device__ __forceinline__ float bf16_hi(uint32_t x) { return __uint_as_float(x & 0xFFFF0000u); }
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
                                          __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-// Element traits: Word is what one lane loads for its DPL output dims.
+// What one lane loads of a value row for its DPL output dims.
 template <typename T, int DPL> struct Elem;
 template <> struct Elem<uint16_t, 2> {
   typedef uint32_t Word;
-  __device__ static float get(Word w, int i) { return i == 0 ? bf16_lo(w) : bf16_hi(w); }
+  __device__ static float get(Word w, int i) {
+    return i == 0 ? __uint_as_float(w << 16) : __uint_as_float(w & 0xFFFF0000u);
+  }
 };
 template <> struct Elem<uint16_t, 1> {
   typedef uint16_t Word;
@@ -77,15 +125,17 @@ __global__ __launch_bounds__(64) void sparse_attn_kernel(
     float scale_log2, int S, int chunk, float* __restrict__ part_o,
     float* __restrict__ part_lse) {
   constexpr bool kBf16 = sizeof(T) == 2;
-  constexpr int DPL = D / 64;  // output dims per lane
+  constexpr int RW = D * (int)sizeof(T) / 4;  // 32-bit words per row
+  constexpr int NV4 = RW / 8;                 // uint4 per half row
+  constexpr int DPL = D / 64;                 // output dims per lane
   typedef Elem<T, DPL> E;
   typedef typename E::Word Word;
-  constexpr int QW = kBf16 ? D / 2 : D;  // 32-bit words per query head row
-  __shared__ __attribute__((aligned(16))) uint32_t q_lds[G * QW];
-  __shared__ float p_lds[64 * G];
-  __shared__ uint32_t row_lds[64];
+  __shared__ uint4 q_lds[G * RW / 4];
+  __shared__ float p_lds[kTile * G];
+  __shared__ uint32_t rows_lds[kSpan];
 
   const int lane = threadIdx.x;
+  const int tl = lane & 31, hf = lane >> 5;
   const int g = blockIdx.x % hkv;
   const int rs = blockIdx.x / hkv;
   const int s = rs % S;
@@ -94,50 +144,82 @@ __global__ __launch_bounds__(64) void sparse_attn_kernel(
   const int a = min(k, s * chunk);
   const int b = min(k, a + chunk);
   const int page_mask = (1 << page_shift) - 1;
+  const int32_t* btr = bt + (size_t)row_req[r] * max_pages;
+  const int32_t* ir = idx + (size_t)r * k;
+  const size_t kv_stride = (size_t)hkv * D;
+  const T* kgroup = kc + (size_t)g * D;
+  const T* vgroup = vc + (size_t)g * D;
 
   {
-    const uint32_t* qsrc =
-        reinterpret_cast<const uint32_t*>(q + ((size_t)r * hq + (size_t)g * G) * D);
-    for (int i = lane; i < G * QW; i += 64) q_lds[i] = qsrc[i];
+    const uint4* qsrc = reinterpret_cast<const uint4*>(q + ((size_t)r * hq + (size_t)g * G) * D);
+    for (int i = lane; i < G * RW / 4; i += 64) q_lds[i] = qsrc[i];
   }
-  __syncthreads();
 
-  float m[G], l[G], o[G][DPL];
+  float m[G], lsum[G], o[G][DPL];
 #pragma unroll
   for (int h = 0; h < G; ++h) {
     m[h] = -INFINITY;
-    l[h] = 0.0f;
+    lsum[h] = 0.0f;
 #pragma unroll
     for (int e = 0; e < DPL; ++e) o[h][e] = 0.0f;
   }
 
-  const int32_t* btr = bt + (size_t)row_req[r] * max_pages;
-  const int32_t* ir = idx + (size_t)r * k;
-  const size_t kv_stride = (size_t)hkv * D;
+  for (int c0 = a; c0 < b; c0 += kSpan) {
+    const int n = min(b - c0, kSpan);
+    // Resolve the span's selected positions to cache rows (0xFFFFFFFF for
+    // padding) once, and find its last selected slot.
+    __syncthreads();  // the previous span's readers are done with rows_lds
+    int last = -1;
+    for (int i = lane; i < n; i += 64) {
+      const int pos = ir[c0 + i];
+      uint32_t row = 0xFFFFFFFFu;
+      if (pos >= 0) {
+        row = ((uint32_t)btr[pos >> page_shift] << page_shift) | (uint32_t)(pos & page_mask);
+        last = i;
+      }
+      rows_lds[i] = row;
+    }
+    last = wave_max_i32(last);
+    __syncthreads();
+    const int ntiles = (last + kTile) / kTile;  // tiles up to the last selected slot
 
-  for (int t0 = a; t0 < b; t0 += 64) {
-    const int slot = t0 + lane;
-    const int pos = slot < b ? ir[slot] : -1;
-    const bool valid = pos >= 0;
-    if (__ballot(valid) == 0) break;
-    uint32_t krow = 0xFFFFFFFFu;
-    if (valid) krow = ((uint32_t)btr[pos >> page_shift] << page_shift) | (uint32_t)(pos & page_mask);
+    // Row ids of tile t for this lane's token (lanes t and t+32 share one).
+    auto tile_row = [&](int t) -> uint32_t {
+      const int i = t * kTile + tl;
+      return i < n ? rows_lds[i] : 0xFFFFFFFFu;
+    };
+    // Loads are unconditional: a padding slot reads cache row 0 and gets
+    // probability 0, so the load counters stay exact.
+    auto load_k = [&](uint32_t row, uint4 (&kv)[NV4]) {
+      const uint32_t rr = row == 0xFFFFFFFFu ? 0u : row;
+      const uint4* kp = reinterpret_cast<const uint4*>(kgroup + (size_t)rr * kv_stride) + hf * NV4;
+#pragma unroll
+      for (int c = 0; c < NV4; ++c) kv[c] = kp[c];
+    };
 
-    float sc[G];
+    uint32_t krow = tile_row(0);
+    uint4 kv[NV4];
+    load_k(krow, kv);
+    for (int t = 0; t < ntiles; ++t) {
+      // V of tile t: one whole row per token, its row id wave-uniform.
+      Word vw[kTile];
 #pragma unroll
-    for (int h = 0; h < G; ++h) sc[h] = 0.0f;
-    if (valid) {
-      const uint4* kp = reinterpret_cast<const uint4*>(kc + (size_t)krow * kv_stride + (size_t)g * D);
-      constexpr int NV = QW / 4;  // uint4 per key row
-      uint4 kv[NV];
-#pragma unroll
-      for (int c = 0; c < NV; ++c) kv[c] = kp[c];
+      for (int j = 0; j < kTile; ++j) {
+        uint32_t rj = (uint32_t)__builtin_amdgcn_readlane((int)krow, j);
+        rj = rj == 0xFFFFFFFFu ? 0u : rj;
+        vw[j] = reinterpret_cast<const Word*>(vgroup + (size_t)rj * kv_stride)[lane];
+      }
+      const bool valid = krow != 0xFFFFFFFFu;
+      const uint32_t krow_next = tile_row(t + 1);
+
+      // Scores for the group's heads (log2 units).
+      float sc[G];
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const uint4* qh = reinterpret_cast<const uint4*>(q_lds + h * QW);
+        const uint4* qh = q_lds + h * (RW / 4) + hf * NV4;
         float acc = 0.0f;
 #pragma unroll
-        for (int c = 0; c < NV; ++c) {
+        for (int c = 0; c < NV4; ++c) {
           const uint4 qv = qh[c];
           if constexpr (kBf16) {
             acc = dot2_bf16(kv[c].x, qv.x, acc);
@@ -151,57 +233,64 @@ __global__ __launch_bounds__(64) void sparse_attn_kernel(
             acc = fmaf(__uint_as_float(kv[c].w), __uint_as_float(qv.w), acc);
           }
         }
-        sc[h] = acc * scale_log2;
+        sc[h] = valid ? add_halves(acc) * scale_log2 : -INFINITY;
       }
-    }
+      // K of tile t+1 in flight while tile t's values are summed.
+      load_k(krow_next, kv);
 
+      // Online softmax with a deferred reference: probabilities are taken
+      // against the running reference m[h]; only when some score exceeds it
+      // by more than 2^kSlack (or on the first tile, m = -inf) is the
+      // reference raised to the true running max and the accumulators
+      // rescaled. The result is the same normalized softmax -- o and the sum
+      // share the reference -- and every probability stays <= 2^kSlack.
+      bool over = false;
 #pragma unroll
-    for (int h = 0; h < G; ++h) {
-      const float mt = wave_max_f32(valid ? sc[h] : -INFINITY);
-      const float mn = fmaxf(m[h], mt);
-      const float alpha = (m[h] == -INFINITY) ? 0.0f : exp2f(m[h] - mn);
-      const float p = valid ? exp2f(sc[h] - mn) : 0.0f;
-      l[h] = l[h] * alpha + wave_sum_f32(p);
-#pragma unroll
-      for (int e = 0; e < DPL; ++e) o[h][e] *= alpha;
-      m[h] = mn;
-      p_lds[lane * G + h] = p;
-    }
-    row_lds[lane] = krow;
-    __syncthreads();
-
-    const T* vbase = vc + (size_t)g * D + (size_t)lane * DPL;
-#pragma unroll 1
-    for (int j0 = 0; j0 < 64; j0 += 16) {
-      Word vw[16];
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
-        const uint32_t rj = row_lds[j0 + jj];
-        if (rj != 0xFFFFFFFFu) vw[jj] = *reinterpret_cast<const Word*>(vbase + (size_t)rj * kv_stride);
-        else vw[jj] = Word{};
-      }
-#pragma unroll
-      for (int jj = 0; jj < 16; ++jj) {
+      for (int h = 0; h < G; ++h) over |= sc[h] > m[h] + kSlack;
+      if (__ballot(over) != 0) {
 #pragma unroll
         for (int h = 0; h < G; ++h) {
-          const float p = p_lds[(j0 + jj) * G + h];
+          const float mn = fmaxf(m[h], wave_max(sc[h]));
+          const float alpha = fast_exp2(m[h] - mn);  // m = -inf: alpha = 0
+          lsum[h] *= alpha;
 #pragma unroll
-          for (int e = 0; e < DPL; ++e) o[h][e] = fmaf(p, E::get(vw[jj], e), o[h][e]);
+          for (int e = 0; e < DPL; ++e) o[h][e] *= alpha;
+          m[h] = mn;
         }
       }
+#pragma unroll
+      for (int h = 0; h < G; ++h) {
+        const float p = fast_exp2(sc[h] - m[h]);  // -inf (padding) -> 0
+        lsum[h] += (hf == 0) ? p : 0.0f;
+        if (hf == 0) p_lds[tl * G + h] = p;
+      }
+      __syncthreads();
+
+#pragma unroll
+      for (int j = 0; j < kTile; ++j) {
+        float pj[G];
+#pragma unroll
+        for (int h = 0; h < G; ++h) pj[h] = p_lds[j * G + h];
+#pragma unroll
+        for (int h = 0; h < G; ++h)
+#pragma unroll
+          for (int e = 0; e < DPL; ++e) o[h][e] = fmaf(pj[h], E::get(vw[j], e), o[h][e]);
+      }
+      __syncthreads();
+      krow = krow_next;
     }
-    __syncthreads();
   }
 
 #pragma unroll
   for (int h = 0; h < G; ++h) {
+    const float l = wave_sum(lsum[h]);
     const size_t head = (size_t)r * hq + (size_t)g * G + h;
-    const bool any = l[h] > 0.0f;
-    const float inv = any ? 1.0f / l[h] : 0.0f;
+    const bool any = l > 0.0f;
+    const float inv = any ? 1.0f / l : 0.0f;
     float* po = part_o + (head * S + s) * D + (size_t)lane * DPL;
 #pragma unroll
     for (int e = 0; e < DPL; ++e) po[e] = o[h][e] * inv;
-    if (lane == 0) part_lse[head * S + s] = any ? (m[h] + __log2f(l[h])) * kLn2 : -INFINITY;
+    if (lane == 0) part_lse[head * S + s] = any ? (m[h] + __log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
@@ -218,13 +307,13 @@ static hipError_t launch_attn_t(const T* q, const T* kc, const T* vc, const int3
   hipLaunchKernelGGL((sparse_attn_kernel<T, D_, G_>), grid, dim3(64), 0, stream, q, kc, vc, bt, \
                      row_req, idx, hkv, k, page_shift, max_pages, sl2, S, chunk, part_o,      \
                      part_lse)
-#define DSA_ATTN_G(D_)                  \
-  switch (G) {                          \
-    case 1: DSA_ATTN(D_, 1); break;     \
-    case 2: DSA_ATTN(D_, 2); break;     \
-    case 4: DSA_ATTN(D_, 4); break;     \
-    case 8: DSA_ATTN(D_, 8); break;     \
-    case 16: DSA_ATTN(D_, 16); break;   \
+#define DSA_ATTN_G(D_)                    \
+  switch (G) {                            \
+    case 1: DSA_ATTN(D_, 1); break;       \
+    case 2: DSA_ATTN(D_, 2); break;       \
+    case 4: DSA_ATTN(D_, 4); break;       \
+    case 8: DSA_ATTN(D_, 8); break;       \
+    case 16: DSA_ATTN(D_, 16); break;     \
     default: return hipErrorInvalidValue; \
   }
   if (d == 128) {

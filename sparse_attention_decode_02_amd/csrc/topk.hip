@@ -104,22 +104,25 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   const float* row = scores + (size_t)r * width;
   const int nchunks = (L + kChunk - 1) / kChunk;
   uint32_t key[kVPT];
+  int nv = 0;  // valid positions among this thread's kVPT in the current chunk
 
+  // Keys of chunk c: positions c*kChunk + tid*kVPT + j; invalid ones read as 0
+  // and are excluded by nv.
   auto load_chunk = [&](int c) {
     const int base = c * kChunk + tid * kVPT;
+    nv = min(kVPT, max(0, L - base));
+    if (nv == kVPT) {
 #pragma unroll
-    for (int j = 0; j < kVPT; j += 4) {
-      const int p = base + j;
-      if (p + 3 < L) {
-        const float4 v = *reinterpret_cast<const float4*>(row + p);
+      for (int j = 0; j < kVPT; j += 4) {
+        const float4 v = *reinterpret_cast<const float4*>(row + base + j);
         key[j] = order_key(v.x);
         key[j + 1] = order_key(v.y);
         key[j + 2] = order_key(v.z);
         key[j + 3] = order_key(v.w);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 4; ++e) key[j + e] = (p + e < L) ? order_key(row[p + e]) : 0u;
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kVPT; ++j) key[j] = (j < nv) ? order_key(row[base + j]) : 0u;
     }
   };
   const bool resident = (nchunks == 1);
@@ -129,13 +132,19 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   uint32_t mx = 0u, mn = 0xFFFFFFFFu;
   for (int c = 0; c < nchunks; ++c) {
     if (!resident) load_chunk(c);
-    const int base = c * kChunk + tid * kVPT;
+    if (nv == kVPT) {
 #pragma unroll
-    for (int j = 0; j < kVPT; ++j) {
-      if (base + j < L) {
+      for (int j = 0; j < kVPT; ++j) {
         mx = max(mx, key[j]);
         mn = min(mn, key[j]);
       }
+    } else {
+#pragma unroll
+      for (int j = 0; j < kVPT; ++j)
+        if (j < nv) {
+          mx = max(mx, key[j]);
+          mn = min(mn, key[j]);
+        }
     }
   }
   mx = wave_max_u32(mx);
@@ -155,8 +164,11 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
   __syncthreads();  // `red` is reused by the scans below
 
   // ---- radix select of the threshold prefix --------------------------------
-  // Candidates are the keys whose bits above `shift` equal `prefix`; `need`
-  // of them still have to be taken, and every key above the prefix is taken.
+  // Candidates are the keys whose bits at and above `shift` equal `prefix`;
+  // `need` of them are still to be taken, and every key above the prefix is
+  // taken. Every key shares the bits above the highest bit where the row's
+  // min and max differ, so the first digit starts there and needs no prefix
+  // test.
   int shift;
   uint32_t prefix;
   uint32_t need = (uint32_t)k;
@@ -167,6 +179,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     shift = 32 - __clz(mx ^ mn);
     prefix = high_bits(mx, shift);
   }
+  bool first = true;
   while (shift > 0) {
     const int nb = min(kDigitBits, shift);
     const int ns = shift - nb;
@@ -176,11 +189,21 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     __syncthreads();
     for (int c = 0; c < nchunks; ++c) {
       if (!resident) load_chunk(c);
-      const int base = c * kChunk + tid * kVPT;
+      if (first && nv == kVPT) {
 #pragma unroll
-      for (int j = 0; j < kVPT; ++j) {
-        if (base + j < L && high_bits(key[j], shift) == prefix)
-          atomicAdd(&hist[(key[j] >> ns) & dmask], 1u);
+        for (int j = 0; j < kVPT; ++j) atomicAdd(&hist[(key[j] >> ns) & dmask], 1u);
+      } else if (first) {
+#pragma unroll
+        for (int j = 0; j < kVPT; ++j)
+          if (j < nv) atomicAdd(&hist[(key[j] >> ns) & dmask], 1u);
+      } else if (nv == kVPT) {
+#pragma unroll
+        for (int j = 0; j < kVPT; ++j)
+          if ((key[j] >> shift) == prefix) atomicAdd(&hist[(key[j] >> ns) & dmask], 1u);
+      } else {
+#pragma unroll
+        for (int j = 0; j < kVPT; ++j)
+          if (j < nv && (key[j] >> shift) == prefix) atomicAdd(&hist[(key[j] >> ns) & dmask], 1u);
       }
     }
     __syncthreads();
@@ -214,41 +237,46 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     prefix = (prefix << nb) | digit;
     shift = ns;
     need -= above;
+    first = false;
     if (cand == need) break;
   }
 
   // ---- ordered emit ---------------------------------------------------------
+  // Each thread marks its keys above the prefix (taken) and equal to it
+  // (taken in position order while `need` lasts), one block scan of the two
+  // counts gives its output offsets, and it walks only its marked keys.
   uint32_t gt_run = 0, eq_run = 0;
   for (int c = 0; c < nchunks; ++c) {
     if (!resident) load_chunk(c);
     const int base = c * kChunk + tid * kVPT;
-    uint32_t ngt = 0, neq = 0;
+    uint32_t gtm = 0u, eqm = 0u;
 #pragma unroll
     for (int j = 0; j < kVPT; ++j) {
-      if (base + j < L) {
-        const uint32_t hb = high_bits(key[j], shift);
-        ngt += hb > prefix;
-        neq += hb == prefix;
-      }
+      const uint32_t hb = key[j] >> shift;
+      gtm |= (uint32_t)(hb > prefix) << j;
+      eqm |= (uint32_t)(hb == prefix) << j;
     }
+    const uint32_t vmask = nv == kVPT ? 0xFFFFFFFFu : ((1u << nv) - 1u);
+    gtm &= vmask;
+    eqm &= vmask;
     uint32_t total;
-    const uint32_t excl = block_exclusive_scan((ngt << 16) | neq, red, &total);
+    const uint32_t excl =
+        block_exclusive_scan(((uint32_t)__popc(gtm) << 16) | (uint32_t)__popc(eqm), red, &total);
     uint32_t g = gt_run + (excl >> 16);
     uint32_t e = eq_run + (excl & 0xFFFFu);
-#pragma unroll
-    for (int j = 0; j < kVPT; ++j) {
-      if (base + j < L) {
-        const uint32_t hb = high_bits(key[j], shift);
-        // Every slot written is < k by construction; the bound keeps a
-        // broken invariant from ever turning into an out-of-row store.
-        if (hb > prefix) {
-          const uint32_t slot = g + min(e, need);
-          if (slot < (uint32_t)k) out[slot] = base + j;
-          ++g;
-        } else if (hb == prefix) {
-          if (e < need && g + e < (uint32_t)k) out[g + e] = base + j;
-          ++e;
-        }
+    uint32_t m = gtm | eqm;
+    while (m) {
+      const int j = __ffs(m) - 1;
+      m &= m - 1u;
+      // Every slot written is < k by construction; the bound keeps a broken
+      // invariant from ever turning into an out-of-row store.
+      if ((gtm >> j) & 1u) {
+        const uint32_t slot = g + min(e, need);
+        if (slot < (uint32_t)k) out[slot] = base + j;
+        ++g;
+      } else {
+        if (e < need && g + e < (uint32_t)k) out[g + e] = base + j;
+        ++e;
       }
     }
     gt_run += total >> 16;

@@ -141,6 +141,7 @@ def _merge_args(**kw):
     (dict(max_pages=0), SHAPE), (dict(page_size=48), SHAPE), (dict(page_size=0), SHAPE),
     (dict(blocks=A, num_blocks=0), SHAPE), (dict(blocks=A, num_blocks=5), SHAPE),
     (dict(num_heads=48), UNSUP), (dict(head_dim=96), UNSUP), (dict(dtype=7), UNSUP),
+    (dict(page_size=8), UNSUP), (dict(page_size=8, dtype=0, num_heads=4, head_dim=32, scores=A + 4), ALIGN),
     (dict(dtype=0, num_heads=65), UNSUP), (dict(dtype=0, head_dim=256), UNSUP),
     (dict(q_idx=A + 2), ALIGN), (dict(k_idx_cache=A + 8), ALIGN), (dict(scores=A + 4), ALIGN),
     (dict(w=A + 2), ALIGN), (dict(blocks=A + 2, num_blocks=2), ALIGN),
