@@ -200,6 +200,20 @@ int dsa_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
                     int page_size, int max_pages, float scale, int num_splits, float* part_o,
                     float* part_lse, dsa_dtype dtype, void* stream);
 
+/*
+ * dsa_sparse_attn_splits: a num_splits for dsa_sparse_attn with these shapes
+ * on the current HIP device -- enough splits that one launch has about two
+ * thirds as many waves as the device runs at once (more splits add partial
+ * traffic and per-wave setup, fewer leave compute units idle), each split
+ * keeping at least 32 slots.
+ * Queries the device (compute-unit count, kernel occupancy); allocates
+ * nothing. Errors: NULL pointer; rows, k or head counts < 1 or
+ * num_q_heads % num_kv_heads != 0 -> DSA_ERR_SHAPE; an unsupported
+ * head_dim / group size / dtype -> DSA_ERR_UNSUPPORTED.
+ */
+int dsa_sparse_attn_splits(int rows, int num_q_heads, int num_kv_heads, int head_dim, int k,
+                           dsa_dtype dtype, int* num_splits);
+
 /* ------------------------------------------------------------------------
  * dsa_merge -- log-sum-exp merge of the split partials (flash decoding,
  * commit "Replace the CuTe decode kernels with two Triton kernels").

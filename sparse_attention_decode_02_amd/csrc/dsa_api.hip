@@ -128,7 +128,8 @@ int dsa_indexer_scores(const void* q_idx, const float* w, const void* k_idx_cach
       (blocks && !aligned(blocks, 4)))
     return DSA_ERR_ALIGN;
   if (rows == 0) return DSA_OK;
-  const int chunk = dtype == DSA_BF16 ? dsa::indexer_chunk_keys(num_blocks, width) : 256;
+  const int chunk =
+      dtype == DSA_BF16 ? dsa::indexer_chunk_keys(num_blocks, width, num_heads, head_dim) : 256;
   if ((long long)num_blocks * ((width + chunk - 1) / chunk) > INT32_MAX) return DSA_ERR_SHAPE;
   hipStream_t st = static_cast<hipStream_t>(stream);
   if (dtype == DSA_BF16)
@@ -177,6 +178,21 @@ int dsa_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
       q, k_cache, v_cache, block_table, row_req, idx, rows, num_q_heads, num_kv_heads, head_dim,
       k, ps, max_pages, scale, num_splits, part_o, part_lse, dtype == DSA_BF16,
       static_cast<hipStream_t>(stream)));
+}
+
+int dsa_sparse_attn_splits(int rows, int num_q_heads, int num_kv_heads, int head_dim, int k,
+                           dsa_dtype dtype, int* num_splits) {
+  if (!num_splits) return DSA_ERR_NULL;
+  if (rows < 1 || num_q_heads < 1 || num_kv_heads < 1 || k < 1 ||
+      num_q_heads % num_kv_heads != 0)
+    return DSA_ERR_SHAPE;
+  const int G = num_q_heads / num_kv_heads;
+  if (!(head_dim == 64 || head_dim == 128) || !(G == 1 || G == 2 || G == 4 || G == 8 || G == 16) ||
+      (dtype != DSA_BF16 && dtype != DSA_F32))
+    return DSA_ERR_UNSUPPORTED;
+  *num_splits = dsa::attn_default_splits(rows, num_q_heads, num_kv_heads, head_dim, k,
+                                         dtype == DSA_BF16);
+  return DSA_OK;
 }
 
 int dsa_merge(const float* part_o, const float* part_lse, int rows, int num_q_heads, int head_dim,

@@ -8,8 +8,17 @@
 
 namespace dsa {
 
-// Keys a workgroup of the indexer covers for one row: a multiple of 128.
-int indexer_chunk_keys(int num_blocks, int width);
+// Workgroups of `kernel` (launched with `block` threads) that the current
+// device runs at once: compute units x resident workgroups per unit. 0 on a
+// HIP error.
+int device_capacity(const void* kernel, int block);
+
+// Keys a workgroup of the bf16 indexer covers for one row (a multiple of 64):
+// the chunks of all blocks fill the device about once, at most 4096 keys.
+int indexer_chunk_keys(int num_blocks, int width, int num_heads, int head_dim);
+
+// Splits of the k slots that fill the device with attention waves about once.
+int attn_default_splits(int rows, int hq, int hkv, int d, int k, bool bf16);
 
 hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kcache,
                                const int32_t* bt, const int32_t* row_req, const int32_t* row_len,

@@ -229,12 +229,33 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_f32_kernel(
   }
 }
 
-int indexer_chunk_keys(int num_blocks, int width) {
-  // Enough workgroups to cover 256 CUs several times over, with chunks that
-  // still amortize the per-row query load.
-  int chunk = 1024;
-  while (chunk > 128 && (long long)num_blocks * ((width + chunk - 1) / chunk) < 2048) chunk >>= 1;
-  return chunk;
+int device_capacity(const void* kernel, int block) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess) return 0;
+  return cus * per_cu;
+}
+
+static const void* indexer_kernel_ptr(int num_heads, int head_dim) {
+  if (num_heads == 64 && head_dim == 128) return (const void*)indexer_mfma_kernel<4, 128>;
+  if (num_heads == 32 && head_dim == 128) return (const void*)indexer_mfma_kernel<2, 128>;
+  if (num_heads == 64 && head_dim == 64) return (const void*)indexer_mfma_kernel<4, 64>;
+  if (num_heads == 32 && head_dim == 64) return (const void*)indexer_mfma_kernel<2, 64>;
+  return nullptr;
+}
+
+int indexer_chunk_keys(int num_blocks, int width, int num_heads, int head_dim) {
+  // One round of workgroups over the device: a kernel whose grid is a small
+  // multiple of what runs at once leaves most of the chip idle in its last
+  // round. Chunks are capped so long rows still spread over many workgroups.
+  const void* kern = indexer_kernel_ptr(num_heads, head_dim);
+  int cap = kern ? device_capacity(kern, kIdxThreads) : 0;
+  if (cap <= 0) cap = 768;
+  const int per_block = max(1, cap / max(1, num_blocks));
+  int chunk = (width + per_block - 1) / per_block;
+  chunk = ((chunk + 63) / 64) * 64;
+  return max(64, min(4096, chunk));
 }
 
 hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kcache,
@@ -242,7 +263,7 @@ hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kc
                                const int32_t* blocks, int num_blocks, float* scores, int width,
                                int num_heads, int head_dim, int page_shift, int max_pages,
                                hipStream_t stream) {
-  const int chunk = indexer_chunk_keys(num_blocks, width);
+  const int chunk = indexer_chunk_keys(num_blocks, width, num_heads, head_dim);
   const int chunks = (width + chunk - 1) / chunk;
   const int total = num_blocks * chunks;
   const auto* q = static_cast<const uint16_t*>(q_idx);

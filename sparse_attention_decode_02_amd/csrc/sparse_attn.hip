@@ -167,17 +167,28 @@ __global__ __launch_bounds__(64) void sparse_attn_kernel(
   for (int c0 = a; c0 < b; c0 += kSpan) {
     const int n = min(b - c0, kSpan);
     // Resolve the span's selected positions to cache rows (0xFFFFFFFF for
-    // padding) once, and find its last selected slot.
+    // padding) once, and find its last selected slot: every position load is
+    // issued, then every block-table load, so the span costs two round trips.
     __syncthreads();  // the previous span's readers are done with rows_lds
+    constexpr int RPL = kSpan / 64;
+    int pos[RPL];
+#pragma unroll
+    for (int u = 0; u < RPL; ++u) {
+      const int i = lane + 64 * u;
+      pos[u] = i < n ? ir[c0 + i] : -1;
+    }
+    uint32_t prow[RPL];
+#pragma unroll
+    for (int u = 0; u < RPL; ++u)
+      prow[u] = pos[u] >= 0 ? (uint32_t)btr[pos[u] >> page_shift] : 0xFFFFFFFFu;
     int last = -1;
-    for (int i = lane; i < n; i += 64) {
-      const int pos = ir[c0 + i];
-      uint32_t row = 0xFFFFFFFFu;
-      if (pos >= 0) {
-        row = ((uint32_t)btr[pos >> page_shift] << page_shift) | (uint32_t)(pos & page_mask);
-        last = i;
-      }
-      rows_lds[i] = row;
+#pragma unroll
+    for (int u = 0; u < RPL; ++u) {
+      const int i = lane + 64 * u;
+      const uint32_t row = pos[u] >= 0 ? ((prow[u] << page_shift) | (uint32_t)(pos[u] & page_mask))
+                                       : 0xFFFFFFFFu;
+      if (i < n) rows_lds[i] = row;
+      if (pos[u] >= 0) last = i;
     }
     last = wave_max_i32(last);
     __syncthreads();
@@ -326,6 +337,31 @@ static hipError_t launch_attn_t(const T* q, const T* kc, const T* vc, const int3
 #undef DSA_ATTN_G
 #undef DSA_ATTN
   return hipGetLastError();
+}
+
+template <typename T>
+static const void* attn_kernel_ptr(int d, int G) {
+#define DSA_ATTN_PTR(D_, G_) \
+  if (d == D_ && G == G_) return (const void*)sparse_attn_kernel<T, D_, G_>;
+  DSA_ATTN_PTR(128, 1) DSA_ATTN_PTR(128, 2) DSA_ATTN_PTR(128, 4) DSA_ATTN_PTR(128, 8)
+  DSA_ATTN_PTR(128, 16) DSA_ATTN_PTR(64, 1) DSA_ATTN_PTR(64, 2) DSA_ATTN_PTR(64, 4)
+  DSA_ATTN_PTR(64, 8) DSA_ATTN_PTR(64, 16)
+#undef DSA_ATTN_PTR
+  return nullptr;
+}
+
+int attn_default_splits(int rows, int hq, int hkv, int d, int k, bool bf16) {
+  const void* kern = bf16 ? attn_kernel_ptr<uint16_t>(d, hq / hkv) : attn_kernel_ptr<float>(d, hq / hkv);
+  int cap = kern ? device_capacity(kern, 64) : 0;
+  if (cap <= 0) cap = 3072;
+  // Waves of one launch ~ two thirds of the device's capacity: longer waves
+  // amortize their prologue (query load, position -> row resolution) better
+  // than a full first round does; each split keeps >= 32 slots.
+  const long long waves = (long long)rows * hkv;
+  const long long target = 2LL * cap / 3;
+  int s = (int)((target + waves / 2) / waves);
+  const int max_s = max(1, k / 32);
+  return max(1, min(s, max_s));
 }
 
 hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, const int32_t* bt,

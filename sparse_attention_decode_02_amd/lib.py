@@ -41,6 +41,7 @@ _SIGS = {
     "dsa_topk": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "dsa_sparse_attn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I, _P]),
     "dsa_merge": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _P]),
+    "dsa_sparse_attn_splits": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_I)]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -186,6 +187,16 @@ def sparse_attn(q, k_cache, v_cache, block_table, row_req, idx, page_size, scale
         _dev(part_o, "part_o", torch.float32), _dev(part_lse, "part_lse", torch.float32), dt,
         _stream(stream)))
     return part_o, part_lse
+
+
+def sparse_attn_splits(rows, num_q_heads, num_kv_heads, head_dim, k, dtype) -> int:
+    """dsa_sparse_attn_splits: the split count that fills the current device."""
+    code = BF16 if dtype == torch.bfloat16 else F32 if dtype == torch.float32 else -1
+    out = _I(0)
+    _check("dsa_sparse_attn_splits", _lib.dsa_sparse_attn_splits(
+        int(rows), int(num_q_heads), int(num_kv_heads), int(head_dim), int(k), code,
+        ctypes.byref(out)))
+    return out.value
 
 
 def merge(part_o, part_lse, out, out_lse=None, stream=None):

@@ -14,15 +14,6 @@ import torch
 from . import lib
 
 
-def default_splits(rows: int, hkv: int, k: int) -> int:
-    """Splits of the k slots per (row, KV group): enough waves to cover the
-    chip (about 4096), and at least 64 slots per split."""
-    s = 1
-    while rows * hkv * s < 4096 and (2 * s) * 64 <= k:
-        s *= 2
-    return s
-
-
 class DsaStep:
     """Buffers and launches for one step of ``inp`` (a StepInputs on a CUDA
     device). ``block_rows`` > 1 groups consecutive rows of a request into
@@ -42,7 +33,8 @@ class DsaStep:
         self.blocks = None
         if block_rows > 1:
             self.blocks = torch.from_numpy(lib.plan_blocks(req, block_rows)).to(dev)
-        self.num_splits = num_splits or default_splits(self.rows, wl.hkv, wl.topk)
+        self.num_splits = num_splits or lib.sparse_attn_splits(
+            self.rows, wl.hq, wl.hkv, wl.d, wl.topk, inp.q.dtype)
         self.scores = torch.empty(self.rows, self.width, dtype=torch.float32, device=dev)
         self.idx = torch.empty(self.rows, wl.topk, dtype=torch.int32, device=dev)
         self.part_o = torch.empty(self.rows, wl.hq, self.num_splits, wl.d, dtype=torch.float32,

@@ -189,3 +189,17 @@ def test_sparse_attn_rejects(kw, code):
 ])
 def test_merge_rejects(kw, code):
     assert lib._lib.dsa_merge(*_merge_args(**kw)) == code
+
+
+@pytest.mark.parametrize("args,code", [
+    ((4, 64, 8, 128, 2048, 1, None), NULL),
+    ((0, 64, 8, 128, 2048, 1, "out"), SHAPE), ((4, 64, 0, 128, 2048, 1, "out"), SHAPE),
+    ((4, 64, 3, 128, 2048, 1, "out"), SHAPE), ((4, 64, 8, 128, 0, 1, "out"), SHAPE),
+    ((4, 64, 8, 96, 2048, 1, "out"), UNSUP), ((4, 24, 8, 128, 2048, 1, "out"), UNSUP),
+    ((4, 64, 8, 128, 2048, 9, "out"), UNSUP),
+])
+def test_attn_splits_rejects(args, code):
+    out = ctypes.c_int(0)
+    a = list(args)
+    a[-1] = None if a[-1] is None else ctypes.byref(out)
+    assert lib._lib.dsa_sparse_attn_splits(*a) == code
