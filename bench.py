@@ -32,6 +32,9 @@ if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
 METRIC = "DSA layer latency (us) + HBM GB/s, B=64 ctx 32k top-k 2048, 1 GPU"
+PROFILE = os.path.join(ROOT, "profiles", "dsa_kernels_decode_b64_ctx32k.json")
+STAGE_SOURCE = {"indexer": "indexer.hip", "topk": "topk.hip", "attention": "sparse_attn.hip",
+                "merge": "merge.hip"}
 HBM_PEAK_GBPS = 8000.0
 PAGES_LAYER_US = 160.0  # one decode layer, batch 64, 32K context, top-k 2048, on GB300 (context)
 
@@ -54,6 +57,24 @@ def algorithmic_bytes(wl, row_len):
         b["attention"] += k_eff * wl.hkv * wl.d * e * 2 + wl.hq * wl.d * e + 4 * wl.topk + 4 * pages
         b["merge"] += wl.hq * wl.d * e
     return b
+
+
+def profiled_traffic(stage, workload_name):
+    """HBM bytes per launch of `stage` from the committed rocprofv3 counter
+    summary, or None when there is none for this workload or the kernel's
+    source changed since the counters were taken."""
+    import hashlib
+    if workload_name != "decode_b64_ctx32k_bf16" or not os.path.exists(PROFILE):
+        return None
+    with open(PROFILE) as f:
+        prof = json.load(f)
+    src = os.path.join(ROOT, "sparse_attention_decode_02_amd", "csrc", STAGE_SOURCE[stage])
+    with open(src, "rb") as f:
+        sha = hashlib.sha256(f.read()).hexdigest()
+    for k in prof["kernels"].values():
+        if k["stage"] == stage and k["source_sha256"] == sha:
+            return int(round(k["hbm_bytes_per_launch"]))
+    return None
 
 
 def _events(torch):
@@ -248,7 +269,7 @@ def main(argv=None):
             "peak": HBM_PEAK_GBPS,
             "unit": "GB/s",
             "frac": round(dom_gbps / HBM_PEAK_GBPS, 4),
-            "traffic": None,
+            "traffic": profiled_traffic(dominant, wl.name),
             "algorithmic_bytes_per_launch": ab[dominant],
         },
     }

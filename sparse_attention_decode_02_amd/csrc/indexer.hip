@@ -97,12 +97,12 @@ __global__ __launch_bounds__(kIdxThreads, 3) void indexer_mfma_kernel(
 
     // Key fragments of the 16-key tile at `base` (base is wave-uniform). The
     // tile lies inside one page (page size >= 16), whose number is one scalar
-    // load. Loads are unconditional -- positions past the row read its last
-    // key and are never stored -- so the load counter stays exact and a
-    // prefetch is never waited on early.
+    // load. Loads are unconditional -- positions past the workgroup's chunk
+    // re-read its last key (a cache hit) and are never stored -- so the load
+    // counter stays exact and a prefetch is never waited on early.
     auto load_tile = [&](int base, bf16x8 (&kf)[KS]) {
-      const int page = btr[min(base, L - 1) >> page_shift];
-      const int s = min(base + kl, L - 1);
+      const int page = btr[min(base, end - 1) >> page_shift];
+      const int s = min(base + kl, end - 1);
       const size_t krow = ((size_t)page << page_shift) | (size_t)(s & page_mask);
       const bf16x8* p = reinterpret_cast<const bf16x8*>(kc + krow * DI + grp * 8);
 #pragma unroll
