@@ -31,10 +31,8 @@
 
 namespace dsa {
 
-constexpr int kTopkThreads = 1024;
-constexpr int kTopkWaves = kTopkThreads / 64;
-constexpr int kVPT = 32;                        // positions per thread per chunk
-constexpr int kChunk = kTopkThreads * kVPT;     // 32768
+constexpr int kTopkThreads = 1024;  // threads of the launched configuration
+constexpr int kVPTDefault = 32;      // positions per thread per chunk
 constexpr int kDigitBits = 12;
 constexpr int kBins = 1 << kDigitBits;
 
@@ -61,6 +59,7 @@ __device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
 }
 
 // Exclusive prefix sum over the block in thread order; *total gets the sum.
+template <int kTopkWaves>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* sh,
                                                          uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -84,10 +83,14 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   return base + incl - v;
 }
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restrict__ scores,
-                                                           const int32_t* __restrict__ row_len,
-                                                           int width, int k,
-                                                           int32_t* __restrict__ idx) {
+template <int kThreads, int kVPT>
+__global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores,
+                                                       const int32_t* __restrict__ row_len,
+                                                       int width, int k,
+                                                       int32_t* __restrict__ idx) {
+  constexpr int kTopkThreads = kThreads;
+  constexpr int kTopkWaves = kThreads / 64;
+  constexpr int kChunk = kThreads * kVPT;
   __shared__ uint32_t hist[kBins];
   __shared__ uint32_t red[2 * kTopkWaves];
   __shared__ uint32_t pick[3];
@@ -215,7 +218,7 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
       if (rank < nbins) local += hist[nbins - 1 - rank];
     }
     uint32_t total;
-    const uint32_t before = block_exclusive_scan(local, red, &total);
+    const uint32_t before = block_exclusive_scan<kTopkWaves>(local, red, &total);
     if (before < need && need <= before + local) {
       uint32_t run = before;
       for (int i = 0; i < bpt; ++i) {
@@ -261,7 +264,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
     eqm &= vmask;
     uint32_t total;
     const uint32_t excl =
-        block_exclusive_scan(((uint32_t)__popc(gtm) << 16) | (uint32_t)__popc(eqm), red, &total);
+        block_exclusive_scan<kTopkWaves>(((uint32_t)__popc(gtm) << 16) | (uint32_t)__popc(eqm), red,
+                                         &total);
     uint32_t g = gt_run + (excl >> 16);
     uint32_t e = eq_run + (excl & 0xFFFFu);
     uint32_t m = gtm | eqm;
@@ -286,8 +290,8 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(const float* __restr
 
 hipError_t launch_topk(const float* scores, const int32_t* row_len, int rows, int width, int k,
                        int32_t* idx, hipStream_t stream) {
-  hipLaunchKernelGGL(topk_kernel, dim3(rows), dim3(kTopkThreads), 0, stream, scores, row_len,
-                     width, k, idx);
+  hipLaunchKernelGGL((topk_kernel<kTopkThreads, kVPTDefault>), dim3(rows), dim3(kTopkThreads), 0,
+                     stream, scores, row_len, width, k, idx);
   return hipGetLastError();
 }
 
