@@ -1,8 +1,9 @@
 """Benchmark of one paged DSA layer step on one MI355X.
 
 A step is the whole hot path over one batch: indexer scores -> top-k ->
-GQA sparse attention (split over the k slots) -> log-sum-exp merge, four
-library calls on one stream. The default workload is batch 64 decode at
+GQA sparse attention (split over the k slots) -> log-sum-exp merge: three
+library calls on one stream (attention and merge fused in
+dsa_sparse_attn_merged), or four with --unfused. The default workload is batch 64 decode at
 context 32768, page 64, 64 query / 8 KV heads of dim 128, indexer 64 x 128,
 top-k 2048, bf16, synthetic inputs drawn on the device (randomly permuted
 page tables). Inputs are resident in HBM before the timed region; W warm-up
@@ -96,8 +97,9 @@ def time_steps(step, steps, warmup, torch):
 
 def time_kernels(step, steps, torch):
     """Average duration of each stage's kernel, HIP events on the launch stream."""
-    stages = [("indexer", step.indexer), ("topk", step.topk), ("attention", step.attention),
-              ("merge", step.merge)]
+    stages = [("indexer", step.indexer), ("topk", step.topk), ("attention", step.attention)]
+    if not step.fused:
+        stages.append(("merge", step.merge))
     evs = {n: [_events(torch) for _ in range(steps)] for n, _ in stages}
     for i in range(steps):
         for n, fn in stages:
@@ -182,6 +184,8 @@ def main(argv=None):
                     help="headline (default), decode, tiny, ragged or mixed")
     ap.add_argument("--splits", type=int, default=0, help="attention splits (0 = default)")
     ap.add_argument("--block-rows", type=int, default=1, help="rows per indexer score block")
+    ap.add_argument("--unfused", action="store_true",
+                    help="attention and merge as two launches (dsa_sparse_attn + dsa_merge)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="oracle time budget for cpu_baseline (0 = skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -216,7 +220,8 @@ def main(argv=None):
     wl = I.WORKLOADS[args.workload]()
     print(f"[bench] generating {wl.name} on the device", file=sys.stderr, flush=True)
     inp = I.generate(wl, "cuda")
-    step = DsaStep(inp, num_splits=args.splits or None, block_rows=args.block_rows)
+    step = DsaStep(inp, num_splits=args.splits or None, block_rows=args.block_rows,
+                   fused=not args.unfused)
     torch.cuda.synchronize()
     print(f"[bench] rows {step.rows} width {step.width} splits {step.num_splits}",
           file=sys.stderr, flush=True)
@@ -226,6 +231,8 @@ def main(argv=None):
     layer_us = ms * 1000.0
     ab = algorithmic_bytes(wl, step.row_len_host)
     total_bytes = sum(ab.values())
+    if step.fused:  # the merged kernel also writes the output
+        ab["attention"] += ab.pop("merge")
     gbps = total_bytes / (layer_us * 1e-6) / 1e9
     dominant = max(("indexer", "attention"), key=lambda n: kern[n])
     dom_gbps = ab[dominant] / (kern[dominant] * 1e-6) / 1e9
@@ -257,6 +264,7 @@ def main(argv=None):
             "indexer": f"{wl.hi}x{wl.di}",
             "attention_splits": step.num_splits,
             "indexer_block_rows": args.block_rows,
+            "attention_merge": "fused" if step.fused else "separate",
         },
         "hbm_gbps": round(gbps, 1),
         "layer_frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),

@@ -215,6 +215,33 @@ int dsa_sparse_attn_splits(int rows, int num_q_heads, int num_kv_heads, int head
                            dsa_dtype dtype, int* num_splits);
 
 /* ------------------------------------------------------------------------
+ * dsa_sparse_attn_merged -- dsa_sparse_attn followed by dsa_merge in one
+ * launch (same commits). The num_splits splits of a (row, KV group) run in
+ * one workgroup and are merged on chip; the split partials never reach
+ * device memory. out / out_lse equal, bit for bit, what dsa_sparse_attn with
+ * the same num_splits followed by dsa_merge writes.
+ *
+ *   q, k_cache, v_cache, block_table, row_req, idx: as for dsa_sparse_attn
+ *   out      device [rows][num_q_heads][head_dim] dtype (bf16 rounds to
+ *            nearest even) (output)
+ *   out_lse  device [rows][num_q_heads] float32 (output), or NULL
+ *
+ * Supported: as dsa_sparse_attn, with num_splits in {1, 2, 4, 8} and
+ * num_splits <= k; out 16-byte aligned.
+ * ------------------------------------------------------------------------ */
+int dsa_sparse_attn_merged(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* row_req, const int32_t* idx,
+                           int rows, int num_q_heads, int num_kv_heads, int head_dim, int k,
+                           int page_size, int max_pages, float scale, int num_splits, void* out,
+                           float* out_lse, dsa_dtype dtype, void* stream);
+
+/* dsa_sparse_attn_merged_splits: dsa_sparse_attn_splits rounded down to a
+ * num_splits dsa_sparse_attn_merged supports (1, 2, 4 or 8). Errors as for
+ * dsa_sparse_attn_splits. */
+int dsa_sparse_attn_merged_splits(int rows, int num_q_heads, int num_kv_heads, int head_dim,
+                                  int k, dsa_dtype dtype, int* num_splits);
+
+/* ------------------------------------------------------------------------
  * dsa_merge -- log-sum-exp merge of the split partials (flash decoding,
  * commit "Replace the CuTe decode kernels with two Triton kernels").
  * For each row r and head h, over the splits s:

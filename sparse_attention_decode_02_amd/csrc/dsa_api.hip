@@ -180,6 +180,50 @@ int dsa_sparse_attn(const void* q, const void* k_cache, const void* v_cache,
       static_cast<hipStream_t>(stream)));
 }
 
+int dsa_sparse_attn_merged(const void* q, const void* k_cache, const void* v_cache,
+                           const int32_t* block_table, const int32_t* row_req, const int32_t* idx,
+                           int rows, int num_q_heads, int num_kv_heads, int head_dim, int k,
+                           int page_size, int max_pages, float scale, int num_splits, void* out,
+                           float* out_lse, dsa_dtype dtype, void* stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !row_req || !idx || !out) return DSA_ERR_NULL;
+  if (rows < 0 || num_q_heads < 1 || num_kv_heads < 1 || k < 1 || max_pages < 1 ||
+      num_splits < 1 || num_splits > k || !isfinite(scale))
+    return DSA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return DSA_ERR_SHAPE;
+  const int ps = pow2_shift(page_size);
+  if (ps < 0) return DSA_ERR_SHAPE;
+  const int G = num_q_heads / num_kv_heads;
+  if (!(head_dim == 64 || head_dim == 128) || !(G == 1 || G == 2 || G == 4 || G == 8 || G == 16) ||
+      !(num_splits == 1 || num_splits == 2 || num_splits == 4 || num_splits == 8))
+    return DSA_ERR_UNSUPPORTED;
+  if (dtype != DSA_BF16 && dtype != DSA_F32) return DSA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||
+      (out_lse && !aligned(out_lse, 4)) || !aligned(block_table, 4) || !aligned(row_req, 4) ||
+      !aligned(idx, 4))
+    return DSA_ERR_ALIGN;
+  if (rows == 0) return DSA_OK;
+  if ((long long)rows * num_kv_heads > INT32_MAX) return DSA_ERR_SHAPE;
+  return launch_status(dsa::launch_sparse_attn_merged(
+      q, k_cache, v_cache, block_table, row_req, idx, rows, num_q_heads, num_kv_heads, head_dim,
+      k, ps, max_pages, scale, num_splits, out, out_lse, dtype == DSA_BF16,
+      static_cast<hipStream_t>(stream)));
+}
+
+int dsa_sparse_attn_merged_splits(int rows, int num_q_heads, int num_kv_heads, int head_dim,
+                                  int k, dsa_dtype dtype, int* num_splits) {
+  if (!num_splits) return DSA_ERR_NULL;
+  if (rows < 1 || num_q_heads < 1 || num_kv_heads < 1 || k < 1 ||
+      num_q_heads % num_kv_heads != 0)
+    return DSA_ERR_SHAPE;
+  const int G = num_q_heads / num_kv_heads;
+  if (!(head_dim == 64 || head_dim == 128) || !(G == 1 || G == 2 || G == 4 || G == 8 || G == 16) ||
+      (dtype != DSA_BF16 && dtype != DSA_F32))
+    return DSA_ERR_UNSUPPORTED;
+  *num_splits = dsa::merged_default_splits(rows, num_q_heads, num_kv_heads, head_dim, k,
+                                           dtype == DSA_BF16);
+  return DSA_OK;
+}
+
 int dsa_sparse_attn_splits(int rows, int num_q_heads, int num_kv_heads, int head_dim, int k,
                            dsa_dtype dtype, int* num_splits) {
   if (!num_splits) return DSA_ERR_NULL;

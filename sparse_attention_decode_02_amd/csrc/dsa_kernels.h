@@ -41,6 +41,15 @@ hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, con
                               int num_splits, float* part_o, float* part_lse, bool bf16,
                               hipStream_t stream);
 
+hipError_t launch_sparse_attn_merged(const void* q, const void* kc, const void* vc,
+                                     const int32_t* bt, const int32_t* row_req, const int32_t* idx,
+                                     int rows, int hq, int hkv, int d, int k, int page_shift,
+                                     int max_pages, float scale, int num_splits, void* out,
+                                     float* out_lse, bool bf16, hipStream_t stream);
+
+// Split count for the merged variant: attn_default_splits rounded down to 1/2/4/8.
+int merged_default_splits(int rows, int hq, int hkv, int d, int k, bool bf16);
+
 hipError_t launch_merge(const float* part_o, const float* part_lse, int rows, int hq, int d,
                         int num_splits, void* out, float* out_lse, bool out_bf16,
                         hipStream_t stream);

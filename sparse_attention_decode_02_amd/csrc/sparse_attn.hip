@@ -5,8 +5,10 @@
 // the upstream Blackwell FP32 probability reduction": probabilities stay fp32
 // through the value reduction).
 //
-// One wave per (row, split, KV group). The split's slots are walked in tiles
-// of 32 tokens:
+// One wave per (row, split, KV group); in the merged variant the splits of one
+// (row, KV group) are the waves of one workgroup and are merged through LDS at
+// the end (no partials in HBM, no second launch). The split's slots are walked
+// in tiles of 32 tokens:
 //   * addresses: a prologue translates up to 512 selected positions through
 //     the block table into cache row ids in LDS (two dependent round trips
 //     per span, not per tile); tiles past the span's last selected slot are
@@ -77,6 +79,21 @@ __device__ __forceinline__ float wave_sum(float v) {
   return (a + b) + (c + d);
 }
 
+// Orders this wave's LDS writes before its later LDS reads (the scratch it
+// syncs on is private to the wave, so no workgroup barrier is needed).
+__device__ __forceinline__ void wave_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);  // quiet NaN
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
 // Max over all 64 lanes of an int, wave-uniform.
 __device__ __forceinline__ int wave_max_i32(int v) {
 #pragma unroll
@@ -117,29 +134,35 @@ template <> struct Elem<float, 1> {
   __device__ static float get(Word w, int) { return w; }
 };
 
-template <typename T, int D, int G>
-__global__ __launch_bounds__(64) void sparse_attn_kernel(
+// FS == 0: one wave per workgroup and split, partials written to HBM.
+// FS > 0: the FS splits of one (row, KV group) are the FS waves of one
+// workgroup, merged through LDS into the final output (see the end).
+template <typename T, int D, int G, int FS>
+__global__ __launch_bounds__(64 * (FS > 0 ? FS : 1), (sizeof(T) == 2 && D * G <= 1024) ? 3 : 2) void sparse_attn_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ row_req,
     const int32_t* __restrict__ idx, int hkv, int k, int page_shift, int max_pages,
     float scale_log2, int S, int chunk, float* __restrict__ part_o,
-    float* __restrict__ part_lse) {
+    float* __restrict__ part_lse, void* __restrict__ out, float* __restrict__ out_lse) {
   constexpr bool kBf16 = sizeof(T) == 2;
   constexpr int RW = D * (int)sizeof(T) / 4;  // 32-bit words per row
   constexpr int NV4 = RW / 8;                 // uint4 per half row
   constexpr int DPL = D / 64;                 // output dims per lane
+  constexpr int NW = FS > 0 ? FS : 1;         // waves per workgroup
   typedef Elem<T, DPL> E;
   typedef typename E::Word Word;
   __shared__ uint4 q_lds[G * RW / 4];
-  __shared__ float p_lds[kTile * G];
-  __shared__ uint32_t rows_lds[kSpan];
+  __shared__ float p_lds_all[NW][kTile * G];
+  __shared__ uint32_t rows_lds_all[NW][kSpan];
 
-  const int lane = threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  const int wave = threadIdx.x >> 6;
   const int tl = lane & 31, hf = lane >> 5;
-  const int g = blockIdx.x % hkv;
-  const int rs = blockIdx.x / hkv;
-  const int s = rs % S;
-  const int r = rs / S;
+  const int g = (FS > 0 ? blockIdx.x : blockIdx.x / S) % hkv;
+  const int r = (FS > 0 ? blockIdx.x : blockIdx.x / S) / hkv;
+  const int s = FS > 0 ? wave : (int)(blockIdx.x % S);
+  float* p_lds = p_lds_all[wave];
+  uint32_t* rows_lds = rows_lds_all[wave];
   const int hq = hkv * G;
   const int a = min(k, s * chunk);
   const int b = min(k, a + chunk);
@@ -152,8 +175,9 @@ __global__ __launch_bounds__(64) void sparse_attn_kernel(
 
   {
     const uint4* qsrc = reinterpret_cast<const uint4*>(q + ((size_t)r * hq + (size_t)g * G) * D);
-    for (int i = lane; i < G * RW / 4; i += 64) q_lds[i] = qsrc[i];
+    for (int i = threadIdx.x; i < G * RW / 4; i += 64 * NW) q_lds[i] = qsrc[i];
   }
+  __syncthreads();  // every wave of the workgroup reads the whole query block
 
   float m[G], lsum[G], o[G][DPL];
 #pragma unroll
@@ -169,7 +193,7 @@ __global__ __launch_bounds__(64) void sparse_attn_kernel(
     // Resolve the span's selected positions to cache rows (0xFFFFFFFF for
     // padding) once, and find its last selected slot: every position load is
     // issued, then every block-table load, so the span costs two round trips.
-    __syncthreads();  // the previous span's readers are done with rows_lds
+    wave_sync();  // this wave's previous span readers are done with rows_lds
     constexpr int RPL = kSpan / 64;
     int pos[RPL];
 #pragma unroll
@@ -191,7 +215,7 @@ __global__ __launch_bounds__(64) void sparse_attn_kernel(
       if (pos[u] >= 0) last = i;
     }
     last = wave_max_i32(last);
-    __syncthreads();
+    wave_sync();
     const int ntiles = (last + kTile) / kTile;  // tiles up to the last selected slot
 
     // Row ids of tile t for this lane's token (lanes t and t+32 share one).
@@ -275,7 +299,7 @@ __global__ __launch_bounds__(64) void sparse_attn_kernel(
         lsum[h] += (hf == 0) ? p : 0.0f;
         if (hf == 0) p_lds[tl * G + h] = p;
       }
-      __syncthreads();
+      wave_sync();
 
 #pragma unroll
       for (int j = 0; j < kTile; ++j) {
@@ -287,37 +311,78 @@ __global__ __launch_bounds__(64) void sparse_attn_kernel(
 #pragma unroll
           for (int e = 0; e < DPL; ++e) o[h][e] = fmaf(pj[h], E::get(vw[j], e), o[h][e]);
       }
-      __syncthreads();
+      wave_sync();
       krow = krow_next;
     }
   }
 
+  if constexpr (FS == 0) {
 #pragma unroll
-  for (int h = 0; h < G; ++h) {
-    const float l = wave_sum(lsum[h]);
-    const size_t head = (size_t)r * hq + (size_t)g * G + h;
-    const bool any = l > 0.0f;
-    const float inv = any ? 1.0f / l : 0.0f;
-    float* po = part_o + (head * S + s) * D + (size_t)lane * DPL;
+    for (int h = 0; h < G; ++h) {
+      const float l = wave_sum(lsum[h]);
+      const size_t head = (size_t)r * hq + (size_t)g * G + h;
+      const bool any = l > 0.0f;
+      const float inv = any ? 1.0f / l : 0.0f;
+      float* po = part_o + (head * S + s) * D + (size_t)lane * DPL;
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) po[e] = o[h][e] * inv;
-    if (lane == 0) part_lse[head * S + s] = any ? (m[h] + __log2f(l)) * kLn2 : -INFINITY;
+      for (int e = 0; e < DPL; ++e) po[e] = o[h][e] * inv;
+      if (lane == 0) part_lse[head * S + s] = any ? (m[h] + __log2f(l)) * kLn2 : -INFINITY;
+    }
+  } else {
+    // The FS split partials go to LDS (the same values the unfused kernel
+    // writes to HBM) and are merged exactly as dsa_merge does -- same
+    // operations in the same split order -- so both paths agree bit for bit.
+    __shared__ float o_lds[FS][G][D];
+    __shared__ float lse_lds[FS][G];
+#pragma unroll
+    for (int h = 0; h < G; ++h) {
+      const float l = wave_sum(lsum[h]);
+      const bool any = l > 0.0f;
+      const float inv = any ? 1.0f / l : 0.0f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o_lds[wave][h][lane * DPL + e] = o[h][e] * inv;
+      if (lane == 0) lse_lds[wave][h] = any ? (m[h] + __log2f(l)) * kLn2 : -INFINITY;
+    }
+    __syncthreads();
+    for (int i = threadIdx.x; i < G * D; i += 64 * FS) {
+      const int h = i / D, e = i - h * D;
+      float M = -INFINITY;
+#pragma unroll
+      for (int u = 0; u < FS; ++u) M = fmaxf(M, lse_lds[u][h]);
+      const bool any = M != -INFINITY;
+      const float Mr = any ? M : 0.0f;
+      float W = 0.0f, acc = 0.0f;
+#pragma unroll
+      for (int u = 0; u < FS; ++u) {
+        const float wgt = __expf(lse_lds[u][h] - Mr);
+        W += wgt;
+        acc = fmaf(wgt, o_lds[u][h][e], acc);
+      }
+      const float invW = any ? 1.0f / W : 0.0f;
+      const float x = acc * invW;
+      const size_t oi = ((size_t)r * hq + (size_t)g * G + h) * D + e;
+      if constexpr (kBf16) static_cast<uint16_t*>(out)[oi] = f32_to_bf16_rne(x);
+      else static_cast<float*>(out)[oi] = x;
+      if (out_lse && e == 0) out_lse[(size_t)r * hq + (size_t)g * G + h] = any ? M + __logf(W) : -INFINITY;
+    }
   }
 }
 
-template <typename T>
+template <typename T, int FS>
 static hipError_t launch_attn_t(const T* q, const T* kc, const T* vc, const int32_t* bt,
                                 const int32_t* row_req, const int32_t* idx, int rows, int hq,
                                 int hkv, int d, int k, int page_shift, int max_pages, float scale,
-                                int S, float* part_o, float* part_lse, hipStream_t stream) {
+                                int S, float* part_o, float* part_lse, void* out, float* out_lse,
+                                hipStream_t stream) {
   const int G = hq / hkv;
   const int chunk = (k + S - 1) / S;
-  const dim3 grid((unsigned)rows * S * hkv);
+  const dim3 grid(FS > 0 ? (unsigned)rows * hkv : (unsigned)rows * S * hkv);
+  const dim3 block(64 * (FS > 0 ? FS : 1));
   const float sl2 = scale * kLog2e;
-#define DSA_ATTN(D_, G_)                                                                     \
-  hipLaunchKernelGGL((sparse_attn_kernel<T, D_, G_>), grid, dim3(64), 0, stream, q, kc, vc, bt, \
-                     row_req, idx, hkv, k, page_shift, max_pages, sl2, S, chunk, part_o,      \
-                     part_lse)
+#define DSA_ATTN(D_, G_)                                                                        \
+  hipLaunchKernelGGL((sparse_attn_kernel<T, D_, G_, FS>), grid, block, 0, stream, q, kc, vc, bt, \
+                     row_req, idx, hkv, k, page_shift, max_pages, sl2, S, chunk, part_o,         \
+                     part_lse, out, out_lse)
 #define DSA_ATTN_G(D_)                    \
   switch (G) {                            \
     case 1: DSA_ATTN(D_, 1); break;       \
@@ -342,7 +407,7 @@ static hipError_t launch_attn_t(const T* q, const T* kc, const T* vc, const int3
 template <typename T>
 static const void* attn_kernel_ptr(int d, int G) {
 #define DSA_ATTN_PTR(D_, G_) \
-  if (d == D_ && G == G_) return (const void*)sparse_attn_kernel<T, D_, G_>;
+  if (d == D_ && G == G_) return (const void*)sparse_attn_kernel<T, D_, G_, 0>;
   DSA_ATTN_PTR(128, 1) DSA_ATTN_PTR(128, 2) DSA_ATTN_PTR(128, 4) DSA_ATTN_PTR(128, 8)
   DSA_ATTN_PTR(128, 16) DSA_ATTN_PTR(64, 1) DSA_ATTN_PTR(64, 2) DSA_ATTN_PTR(64, 4)
   DSA_ATTN_PTR(64, 8) DSA_ATTN_PTR(64, 16)
@@ -370,12 +435,56 @@ hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, con
                               int num_splits, float* part_o, float* part_lse, bool bf16,
                               hipStream_t stream) {
   if (bf16)
-    return launch_attn_t(static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
-                         static_cast<const uint16_t*>(vc), bt, row_req, idx, rows, hq, hkv, d, k,
-                         page_shift, max_pages, scale, num_splits, part_o, part_lse, stream);
-  return launch_attn_t(static_cast<const float*>(q), static_cast<const float*>(kc),
-                       static_cast<const float*>(vc), bt, row_req, idx, rows, hq, hkv, d, k,
-                       page_shift, max_pages, scale, num_splits, part_o, part_lse, stream);
+    return launch_attn_t<uint16_t, 0>(
+        static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(kc),
+        static_cast<const uint16_t*>(vc), bt, row_req, idx, rows, hq, hkv, d, k, page_shift,
+        max_pages, scale, num_splits, part_o, part_lse, nullptr, nullptr, stream);
+  return launch_attn_t<float, 0>(static_cast<const float*>(q), static_cast<const float*>(kc),
+                                 static_cast<const float*>(vc), bt, row_req, idx, rows, hq, hkv, d,
+                                 k, page_shift, max_pages, scale, num_splits, part_o, part_lse,
+                                 nullptr, nullptr, stream);
+}
+
+template <typename T>
+static hipError_t launch_merged_t(const void* q, const void* kc, const void* vc, const int32_t* bt,
+                                  const int32_t* row_req, const int32_t* idx, int rows, int hq,
+                                  int hkv, int d, int k, int page_shift, int max_pages, float scale,
+                                  int S, void* out, float* out_lse, hipStream_t stream) {
+  const T* q_ = static_cast<const T*>(q);
+  const T* k_ = static_cast<const T*>(kc);
+  const T* v_ = static_cast<const T*>(vc);
+#define DSA_MERGED(FS_)                                                                         \
+  return launch_attn_t<T, FS_>(q_, k_, v_, bt, row_req, idx, rows, hq, hkv, d, k, page_shift,   \
+                               max_pages, scale, S, nullptr, nullptr, out, out_lse, stream)
+  switch (S) {
+    case 1: DSA_MERGED(1);
+    case 2: DSA_MERGED(2);
+    case 4: DSA_MERGED(4);
+    case 8: DSA_MERGED(8);
+    default: return hipErrorInvalidValue;
+  }
+#undef DSA_MERGED
+}
+
+hipError_t launch_sparse_attn_merged(const void* q, const void* kc, const void* vc,
+                                     const int32_t* bt, const int32_t* row_req, const int32_t* idx,
+                                     int rows, int hq, int hkv, int d, int k, int page_shift,
+                                     int max_pages, float scale, int num_splits, void* out,
+                                     float* out_lse, bool bf16, hipStream_t stream) {
+  if (bf16)
+    return launch_merged_t<uint16_t>(q, kc, vc, bt, row_req, idx, rows, hq, hkv, d, k, page_shift,
+                                     max_pages, scale, num_splits, out, out_lse, stream);
+  return launch_merged_t<float>(q, kc, vc, bt, row_req, idx, rows, hq, hkv, d, k, page_shift,
+                                max_pages, scale, num_splits, out, out_lse, stream);
+}
+
+int merged_default_splits(int rows, int hq, int hkv, int d, int k, bool bf16) {
+  // The fused kernel runs the same waves as the split kernel; round the split
+  // count to a supported workgroup size (1, 2, 4 or 8 waves).
+  const int s = attn_default_splits(rows, hq, hkv, d, k, bf16);
+  int f = 1;
+  while (f * 2 <= s && f * 2 <= 8 && f * 2 <= k) f *= 2;
+  return f;
 }
 
 }  // namespace dsa

@@ -42,6 +42,8 @@ _SIGS = {
     "dsa_sparse_attn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I, _P]),
     "dsa_merge": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _P]),
     "dsa_sparse_attn_splits": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_I)]),
+    "dsa_sparse_attn_merged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I, _P]),
+    "dsa_sparse_attn_merged_splits": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_I)]),
 }
 for _name, (_res, _args) in _SIGS.items():
     _fn = getattr(_lib, _name)
@@ -194,6 +196,35 @@ def sparse_attn_splits(rows, num_q_heads, num_kv_heads, head_dim, k, dtype) -> i
     code = BF16 if dtype == torch.bfloat16 else F32 if dtype == torch.float32 else -1
     out = _I(0)
     _check("dsa_sparse_attn_splits", _lib.dsa_sparse_attn_splits(
+        int(rows), int(num_q_heads), int(num_kv_heads), int(head_dim), int(k), code,
+        ctypes.byref(out)))
+    return out.value
+
+
+def sparse_attn_merged(q, k_cache, v_cache, block_table, row_req, idx, page_size, scale,
+                       num_splits, out, out_lse=None, stream=None):
+    """dsa_sparse_attn_merged: attention and merge in one launch; writes out
+    [rows][Hq][d] (and out_lse [rows][Hq] if given)."""
+    rows, hq, d = q.shape
+    hkv = k_cache.shape[2]
+    dt = _dtype_code(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype or out.dtype != q.dtype:
+        raise TypeError("q, k_cache, v_cache and out dtypes differ")
+    _check("dsa_sparse_attn_merged", _lib.dsa_sparse_attn_merged(
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_table, "block_table", torch.int32), _dev(row_req, "row_req", torch.int32),
+        _dev(idx, "idx", torch.int32), rows, hq, hkv, d, int(idx.shape[1]), int(page_size),
+        int(block_table.shape[1]), float(scale), int(num_splits), _dev(out, "out"),
+        None if out_lse is None else _dev(out_lse, "out_lse", torch.float32), dt,
+        _stream(stream)))
+    return out, out_lse
+
+
+def sparse_attn_merged_splits(rows, num_q_heads, num_kv_heads, head_dim, k, dtype) -> int:
+    """dsa_sparse_attn_merged_splits: the split count for dsa_sparse_attn_merged."""
+    code = BF16 if dtype == torch.bfloat16 else F32 if dtype == torch.float32 else -1
+    out = _I(0)
+    _check("dsa_sparse_attn_merged_splits", _lib.dsa_sparse_attn_merged_splits(
         int(rows), int(num_q_heads), int(num_kv_heads), int(head_dim), int(k), code,
         ctypes.byref(out)))
     return out.value

@@ -1,5 +1,6 @@
 """One paged DSA step on the GPU: the row plan, the buffers between the stages,
-and the four library calls in order on one stream.
+and the library calls in order on one stream (four, or three with the
+attention and merge fused).
 
 torch supplies only the device memory and the stream; the row plan comes
 from the library's host entry points and every stage runs in its kernels.
@@ -17,9 +18,11 @@ from . import lib
 class DsaStep:
     """Buffers and launches for one step of ``inp`` (a StepInputs on a CUDA
     device). ``block_rows`` > 1 groups consecutive rows of a request into
-    score blocks for the indexer."""
+    score blocks for the indexer. ``fused`` runs attention and the merge as
+    one launch (dsa_sparse_attn_merged) instead of two."""
 
-    def __init__(self, inp, num_splits: int | None = None, block_rows: int = 1):
+    def __init__(self, inp, num_splits: int | None = None, block_rows: int = 1,
+                 fused: bool = False):
         wl = inp.wl
         dev = inp.q.device
         self.inp = inp
@@ -33,13 +36,16 @@ class DsaStep:
         self.blocks = None
         if block_rows > 1:
             self.blocks = torch.from_numpy(lib.plan_blocks(req, block_rows)).to(dev)
-        self.num_splits = num_splits or lib.sparse_attn_splits(
-            self.rows, wl.hq, wl.hkv, wl.d, wl.topk, inp.q.dtype)
+        self.fused = fused
+        splits_of = lib.sparse_attn_merged_splits if fused else lib.sparse_attn_splits
+        self.num_splits = num_splits or splits_of(self.rows, wl.hq, wl.hkv, wl.d, wl.topk,
+                                                  inp.q.dtype)
         self.scores = torch.empty(self.rows, self.width, dtype=torch.float32, device=dev)
         self.idx = torch.empty(self.rows, wl.topk, dtype=torch.int32, device=dev)
-        self.part_o = torch.empty(self.rows, wl.hq, self.num_splits, wl.d, dtype=torch.float32,
+        parts = 0 if fused else self.rows
+        self.part_o = torch.empty(parts, wl.hq, self.num_splits, wl.d, dtype=torch.float32,
                                   device=dev)
-        self.part_lse = torch.empty(self.rows, wl.hq, self.num_splits, dtype=torch.float32,
+        self.part_lse = torch.empty(parts, wl.hq, self.num_splits, dtype=torch.float32,
                                     device=dev)
         self.out = torch.empty(self.rows, wl.hq, wl.d, dtype=inp.q.dtype, device=dev)
         self.out_lse = torch.empty(self.rows, wl.hq, dtype=torch.float32, device=dev)
@@ -55,11 +61,18 @@ class DsaStep:
 
     def attention(self, stream=None):
         i = self.inp
+        if self.fused:
+            lib.sparse_attn_merged(i.q, i.k_cache, i.v_cache, i.block_table, self.row_req,
+                                   self.idx, self.wl.page, self.wl.attn_scale, self.num_splits,
+                                   self.out, self.out_lse, stream=stream)
+            return
         lib.sparse_attn(i.q, i.k_cache, i.v_cache, i.block_table, self.row_req, self.idx,
                         self.wl.page, self.wl.attn_scale, self.num_splits, self.part_o,
                         self.part_lse, stream=stream)
 
     def merge(self, stream=None):
+        if self.fused:
+            return  # done by the attention launch
         lib.merge(self.part_o, self.part_lse, self.out, self.out_lse, stream=stream)
 
     def run(self, stream=None):

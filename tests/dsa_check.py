@@ -20,8 +20,8 @@ CANARY = 0x7FBADBAD  # a NaN bit pattern pre-filled into the score buffer
 TOL = {"bf16": (2e-2, 1e-3), "f32": (1e-5, 1e-5)}
 
 
-def run_step(inp, num_splits=None, block_rows=1, canary=True):
-    step = DsaStep(inp, num_splits=num_splits, block_rows=block_rows)
+def run_step(inp, num_splits=None, block_rows=1, canary=True, fused=False):
+    step = DsaStep(inp, num_splits=num_splits, block_rows=block_rows, fused=fused)
     if canary:
         step.scores.view(torch.int32).fill_(CANARY)
     step.run()
@@ -76,12 +76,14 @@ def check_row(step, r):
     assert bool((tail == CANARY).all()), f"row {r}: a score past the row length was written"
     gi = step.idx[r].cpu().numpy()
     assert np.array_equal(gi, idx), f"row {r}: indices differ at {np.flatnonzero(gi != idx)[:8]}"
-    gpo = _host(step.part_o[r])
-    gpl = _host(step.part_lse[r])
-    e_po = float(np.abs(gpo - po).max()) if po.size else 0.0
-    fin = np.isfinite(pl)
-    assert np.array_equal(np.isfinite(gpl), fin), f"row {r}: empty splits differ"
-    e_pl = float(np.abs(gpl[fin] - pl[fin]).max()) if fin.any() else 0.0
+    e_po = e_pl = 0.0
+    if not step.fused:
+        gpo = _host(step.part_o[r])
+        gpl = _host(step.part_lse[r])
+        e_po = float(np.abs(gpo - po).max()) if po.size else 0.0
+        fin = np.isfinite(pl)
+        assert np.array_equal(np.isfinite(gpl), fin), f"row {r}: empty splits differ"
+        e_pl = float(np.abs(gpl[fin] - pl[fin]).max()) if fin.any() else 0.0
     go = _host(step.out[r])
     gl = _host(step.out_lse[r])
     e_o = float(np.abs(go - o).max())

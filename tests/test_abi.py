@@ -203,3 +203,19 @@ def test_attn_splits_rejects(args, code):
     a = list(args)
     a[-1] = None if a[-1] is None else ctypes.byref(out)
     assert lib._lib.dsa_sparse_attn_splits(*a) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(out=None), NULL), (dict(idx=None), NULL),
+    (dict(rows=-1), SHAPE), (dict(hkv=3), SHAPE), (dict(num_splits=0), SHAPE),
+    (dict(k=2, num_splits=4), SHAPE), (dict(scale=float("nan")), SHAPE),
+    (dict(num_splits=3), UNSUP), (dict(num_splits=16), UNSUP), (dict(d=96), UNSUP),
+    (dict(out=A + 2), ALIGN), (dict(out_lse=A + 2), ALIGN), (dict(q=A + 4), ALIGN),
+    (dict(rows=0), OK),
+])
+def test_merged_rejects(kw, code):
+    a = dict(q=A, k_cache=A, v_cache=A, block_table=A, row_req=A, idx=A, rows=4, hq=64, hkv=8,
+             d=128, k=2048, page_size=64, max_pages=8, scale=0.088, num_splits=4, out=A,
+             out_lse=A, dtype=1, stream=None)
+    a.update(kw)
+    assert lib._lib.dsa_sparse_attn_merged(*a.values()) == code

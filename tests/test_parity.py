@@ -91,6 +91,36 @@ def test_split_counts(S):
         check_row(step, r)
 
 
+@pytest.mark.parametrize("S", [1, 2, 4, 8])
+def test_merged_matches_split_then_merge_bitwise(S):
+    """dsa_sparse_attn_merged writes exactly what dsa_sparse_attn + dsa_merge
+    write, and both match the oracle."""
+    _say(f"merged attention, splits {S}")
+    inp = _host_inputs(_small_mixed(seed=13))
+    two = run_step(inp, num_splits=S)
+    one = run_step(inp, num_splits=S, fused=True)
+    assert torch.equal(one.idx, two.idx)
+    assert torch.equal(one.out.view(torch.int16), two.out.view(torch.int16))
+    assert torch.equal(one.out_lse.view(torch.int32), two.out_lse.view(torch.int32))
+    for r in (0, 36, 40, one.rows - 1):
+        check_row(one, r)
+
+
+@pytest.mark.parametrize("v", [("f32", 16, 4, 1, 64, 4, 32, 16), ("bf16", 32, 32, 2, 128, 64, 128, 64),
+                               ("bf16", 16, 16, 4, 64, 32, 64, 128)], ids=lambda v: "-".join(map(str, v)))
+def test_merged_shapes(v):
+    dt, page, hq, hkv, d, hi, di, topk = v
+    wl = I.custom(I.tiny(), name="variant", dtype=dt, page=page, hq=hq, hkv=hkv, d=d, hi=hi,
+                  di=di, topk=topk, prior=(3, 150, 700, 40), new=(1, 1, 1, 6), seed=77)
+    inp = _host_inputs(wl)
+    for S in (1, 2, 4):
+        two = run_step(inp, num_splits=S)
+        one = run_step(inp, num_splits=S, fused=True)
+        dtv = torch.int16 if dt == "bf16" else torch.int32
+        assert torch.equal(one.out.view(dtv), two.out.view(dtv)), S
+        _check_all(one)
+
+
 VARIANTS = [
     # dtype, page, hq, hkv, d, hi, di, topk
     ("bf16", 64, 8, 8, 128, 32, 128, 64),
@@ -219,7 +249,7 @@ def test_determinism():
 def _full(wl, rows_fn):
     _say(f"{wl.name}: generating on the device")
     inp = I.generate(wl, "cuda")
-    step = run_step(inp)
+    step = run_step(inp, fused=True)  # the launch configuration bench.py times
     _say(f"  rows {step.rows}, width {step.width}, splits {step.num_splits}")
     check_properties(step)
     rows = rows_fn(step)
