@@ -10,7 +10,9 @@
 // (heads as rows, 16 per head tile; keys as columns). Four lanes share a key
 // and read 64 contiguous bytes of its row per MFMA step; three key tiles
 // rotate through registers so two are in flight while one is on the matrix
-// cores. After the MFMAs a lane holds 4 consecutive heads of its key per head
+// cores. The query fragments are read from LDS for every tile rather than
+// held in registers, which leaves room for four waves per SIMD. After the
+// MFMAs a lane holds 4 consecutive heads of its key per head
 // tile; ReLU, the head weight and the head sum run in fp32 registers and two
 // row swaps (v_permlane16_swap, v_permlane32_swap) finish the key.
 // Products of bf16 are exact and the configs' dyadic integers accumulate
@@ -53,7 +55,7 @@ __device__ __forceinline__ float sum_rows(float x) {
 // kk*32 + g*8 + e for both operands, so the four lanes of a key read 64
 // contiguous bytes of its row per step.
 template <int HT, int DI>
-__global__ __launch_bounds__(kIdxThreads, 3) void indexer_mfma_kernel(
+__global__ __launch_bounds__(kIdxThreads, 4) void indexer_mfma_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w,
     const uint16_t* __restrict__ kc, const int32_t* __restrict__ bt,
     const int32_t* __restrict__ row_req, const int32_t* __restrict__ row_len,
@@ -134,24 +136,25 @@ __global__ __launch_bounds__(kIdxThreads, 3) void indexer_mfma_kernel(
     }
     __syncthreads();
 
-    bf16x8 qf[HT][KS];
     float4 wr[HT];
 #pragma unroll
-    for (int t = 0; t < HT; ++t) {
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk)
-        qf[t][kk] = *reinterpret_cast<const bf16x8*>(&q_lds[(t * 16 + kl) * QST + kk * 32 + grp * 8]);
-      wr[t] = *reinterpret_cast<const float4*>(&w_lds[t * 16 + grp * 4]);
-    }
+    for (int t = 0; t < HT; ++t) wr[t] = *reinterpret_cast<const float4*>(&w_lds[t * 16 + grp * 4]);
+    const int qoff0 = kl * QST + grp * 8;
 
     auto score_tile = [&](int base, const bf16x8 (&kf)[KS]) {
+      // The empty asm makes the LDS offset opaque, so the compiler cannot hoist
+      // the query reads out of the tile loop into registers.
+      int qoff = qoff0;
+      asm volatile("" : "+v"(qoff));
       float part = 0.0f;
 #pragma unroll
       for (int t = 0; t < HT; ++t) {
         f32x4 acc = {};
 #pragma unroll
-        for (int kk = 0; kk < KS; ++kk)
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[t][kk], kf[kk], acc, 0, 0, 0);
+        for (int kk = 0; kk < KS; ++kk) {
+          const bf16x8 qv = *reinterpret_cast<const bf16x8*>(&q_lds[t * 16 * QST + kk * 32 + qoff]);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qv, kf[kk], acc, 0, 0, 0);
+        }
         part = fmaf(wr[t].x, relu(acc[0]), part);
         part = fmaf(wr[t].y, relu(acc[1]), part);
         part = fmaf(wr[t].z, relu(acc[2]), part);
@@ -251,7 +254,7 @@ int indexer_chunk_keys(int num_blocks, int width, int num_heads, int head_dim) {
   // round. Chunks are capped so long rows still spread over many workgroups.
   const void* kern = indexer_kernel_ptr(num_heads, head_dim);
   int cap = kern ? device_capacity(kern, kIdxThreads) : 0;
-  if (cap <= 0) cap = 768;
+  if (cap <= 0) cap = 1024;
   const int per_block = max(1, cap / max(1, num_blocks));
   int chunk = (width + per_block - 1) / per_block;
   chunk = ((chunk + 63) / 64) * 64;
