@@ -249,16 +249,20 @@ static const void* indexer_kernel_ptr(int num_heads, int head_dim) {
 }
 
 int indexer_chunk_keys(int num_blocks, int width, int num_heads, int head_dim) {
-  // One round of workgroups over the device: a kernel whose grid is a small
-  // multiple of what runs at once leaves most of the chip idle in its last
-  // round. Chunks are capped so long rows still spread over many workgroups.
+  // About one round of workgroups over the device: a kernel whose grid is a
+  // small multiple of what runs at once leaves most of the chip idle in its
+  // last round. Chunks are capped so that long rows spread over many
+  // workgroups: with fewer blocks than the device holds, ragged lengths leave
+  // a few long rows as the tail, so the cap is 1024 keys; with more, 2048
+  // (the per-workgroup query load is amortized over more keys).
   const void* kern = indexer_kernel_ptr(num_heads, head_dim);
   int cap = kern ? device_capacity(kern, kIdxThreads) : 0;
   if (cap <= 0) cap = 1024;
   const int per_block = max(1, cap / max(1, num_blocks));
+  const int max_chunk = per_block > 1 ? 1024 : 2048;
   int chunk = (width + per_block - 1) / per_block;
   chunk = ((chunk + 63) / 64) * 64;
-  return max(64, min(4096, chunk));
+  return max(64, min(max_chunk, chunk));
 }
 
 hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kcache,

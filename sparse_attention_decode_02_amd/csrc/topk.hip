@@ -46,29 +46,51 @@ __device__ __forceinline__ uint32_t high_bits(uint32_t key, int shift) {
   return shift >= 32 ? 0u : (key >> shift);
 }
 
-__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = max(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, 0xF, 0xF, true);
 }
 
-__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
-#pragma unroll
-  for (int o = 32; o > 0; o >>= 1) v = min(v, (uint32_t)__shfl_xor((int)v, o));
-  return v;
+__device__ __forceinline__ uint32_t lane_u32(uint32_t v, int l) {
+  return (uint32_t)__builtin_amdgcn_readlane((int)v, l);
+}
+
+// Max and min over the wave, wave-uniform: butterflies inside each 16-lane
+// row (quad permutes, half-row and row mirrors), then the four row results.
+__device__ __forceinline__ void wave_max_min(uint32_t& mx, uint32_t& mn) {
+  mx = max(mx, dpp_u32<0xB1>(mx));  // quad_perm [1,0,3,2]
+  mn = min(mn, dpp_u32<0xB1>(mn));
+  mx = max(mx, dpp_u32<0x4E>(mx));  // quad_perm [2,3,0,1]
+  mn = min(mn, dpp_u32<0x4E>(mn));
+  mx = max(mx, dpp_u32<0x141>(mx));  // row_half_mirror
+  mn = min(mn, dpp_u32<0x141>(mn));
+  mx = max(mx, dpp_u32<0x140>(mx));  // row_mirror
+  mn = min(mn, dpp_u32<0x140>(mn));
+  mx = max(max(lane_u32(mx, 0), lane_u32(mx, 16)), max(lane_u32(mx, 32), lane_u32(mx, 48)));
+  mn = min(min(lane_u32(mn, 0), lane_u32(mn, 16)), min(lane_u32(mn, 32), lane_u32(mn, 48)));
+}
+
+// Inclusive prefix sum over the wave in lane order: shifts by 1, 2, 4, 8
+// inside each 16-lane row (lanes shifted in from outside the row read 0),
+// then the totals of the rows below.
+__device__ __forceinline__ uint32_t wave_inclusive_scan(uint32_t x) {
+  x += dpp_u32<0x111>(x);  // row_shr:1
+  x += dpp_u32<0x112>(x);  // row_shr:2
+  x += dpp_u32<0x114>(x);  // row_shr:4
+  x += dpp_u32<0x118>(x);  // row_shr:8
+  const int row = (threadIdx.x & 63) >> 4;
+  const uint32_t r0 = lane_u32(x, 15), r1 = lane_u32(x, 31), r2 = lane_u32(x, 47);
+  return x + (row >= 1 ? r0 : 0u) + (row >= 2 ? r1 : 0u) + (row >= 3 ? r2 : 0u);
 }
 
 // Exclusive prefix sum over the block in thread order; *total gets the sum.
+// `sh` holds one word per wave; the caller gives each scan a slot that no
+// other scan touches until a later barrier, so no barrier is needed after it.
 template <int kTopkWaves>
 __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* sh,
                                                          uint32_t* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  uint32_t incl = v;
-#pragma unroll
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t n = (uint32_t)__shfl_up((int)incl, o);
-    if (lane >= o) incl += n;
-  }
+  const uint32_t incl = wave_inclusive_scan(v);
   if (lane == 63) sh[wave] = incl;
   __syncthreads();
   uint32_t base = 0, tot = 0;
@@ -78,7 +100,6 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
     base += (i < wave) ? x : 0u;
     tot += x;
   }
-  __syncthreads();
   *total = tot;
   return base + incl - v;
 }
@@ -91,7 +112,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   constexpr int kTopkThreads = kThreads;
   constexpr int kTopkWaves = kThreads / 64;
   constexpr int kChunk = kThreads * kVPT;
-  __shared__ uint32_t hist[kBins];
+  __shared__ uint32_t hist[2][kBins];  // alternate passes: one fills while the other is cleared
+  __shared__ uint32_t scan_sh[4][kTopkWaves];  // per-wave words of the block scans, by use
   __shared__ uint32_t red[2 * kTopkWaves];
   __shared__ uint32_t pick[3];
 
@@ -130,6 +152,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   };
   const bool resident = (nchunks == 1);
   if (resident) load_chunk(0);
+  for (int i = tid; i < kBins; i += kTopkThreads) hist[0][i] = 0u;  // while the keys arrive
 
   // ---- min / max over the row --------------------------------------------
   uint32_t mx = 0u, mn = 0xFFFFFFFFu;
@@ -150,8 +173,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
         }
     }
   }
-  mx = wave_max_u32(mx);
-  mn = wave_min_u32(mn);
+  wave_max_min(mx, mn);
   if (lane == 0) {
     red[wave] = mx;
     red[kTopkWaves + wave] = mn;
@@ -164,7 +186,6 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     mx = max(mx, red[i]);
     mn = min(mn, red[kTopkWaves + i]);
   }
-  __syncthreads();  // `red` is reused by the scans below
 
   // ---- radix select of the threshold prefix --------------------------------
   // Candidates are the keys whose bits at and above `shift` equal `prefix`;
@@ -182,65 +203,74 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     shift = 32 - __clz(mx ^ mn);
     prefix = high_bits(mx, shift);
   }
+  // Three barriers per pass: after the histogram, inside the bin scan, and
+  // after the pick. The next pass's histogram buffer is cleared while this
+  // one is read, and every scan has its own per-wave words.
   bool first = true;
+  int hb = 0;
   while (shift > 0) {
     const int nb = min(kDigitBits, shift);
     const int ns = shift - nb;
     const int nbins = 1 << nb;
     const uint32_t dmask = (uint32_t)nbins - 1u;
-    for (int i = tid; i < nbins; i += kTopkThreads) hist[i] = 0u;
-    __syncthreads();
+    uint32_t* h = hist[hb];
     for (int c = 0; c < nchunks; ++c) {
       if (!resident) load_chunk(c);
       if (first && nv == kVPT) {
 #pragma unroll
-        for (int j = 0; j < kVPT; ++j) atomicAdd(&hist[(key[j] >> ns) & dmask], 1u);
+        for (int j = 0; j < kVPT; ++j) atomicAdd(&h[(key[j] >> ns) & dmask], 1u);
       } else if (first) {
 #pragma unroll
         for (int j = 0; j < kVPT; ++j)
-          if (j < nv) atomicAdd(&hist[(key[j] >> ns) & dmask], 1u);
+          if (j < nv) atomicAdd(&h[(key[j] >> ns) & dmask], 1u);
       } else if (nv == kVPT) {
 #pragma unroll
         for (int j = 0; j < kVPT; ++j)
-          if ((key[j] >> shift) == prefix) atomicAdd(&hist[(key[j] >> ns) & dmask], 1u);
+          if ((key[j] >> shift) == prefix) atomicAdd(&h[(key[j] >> ns) & dmask], 1u);
       } else {
 #pragma unroll
         for (int j = 0; j < kVPT; ++j)
-          if (j < nv && (key[j] >> shift) == prefix) atomicAdd(&hist[(key[j] >> ns) & dmask], 1u);
+          if (j < nv && (key[j] >> shift) == prefix) atomicAdd(&h[(key[j] >> ns) & dmask], 1u);
       }
     }
+    // The other buffer was last read before the previous pass's final barrier.
+    for (int i = tid; i < kBins; i += kTopkThreads) hist[hb ^ 1][i] = 0u;
     __syncthreads();
     // Bins in descending digit order; thread t owns ranks [t*bpt, t*bpt+bpt).
+    constexpr int kMaxBpt = (kBins + kTopkThreads - 1) / kTopkThreads;
     const int bpt = (nbins + kTopkThreads - 1) / kTopkThreads;
+    uint32_t cnt[kMaxBpt];
     uint32_t local = 0;
-    for (int i = 0; i < bpt; ++i) {
+#pragma unroll
+    for (int i = 0; i < kMaxBpt; ++i) {
       const int rank = tid * bpt + i;
-      if (rank < nbins) local += hist[nbins - 1 - rank];
+      cnt[i] = (i < bpt && rank < nbins) ? h[nbins - 1 - rank] : 0u;
+      local += cnt[i];
     }
     uint32_t total;
-    const uint32_t before = block_exclusive_scan<kTopkWaves>(local, red, &total);
+    const uint32_t before = block_exclusive_scan<kTopkWaves>(local, scan_sh[hb], &total);
     if (before < need && need <= before + local) {
       uint32_t run = before;
-      for (int i = 0; i < bpt; ++i) {
-        const int rank = tid * bpt + i;
-        if (rank >= nbins) break;
-        const uint32_t hb = hist[nbins - 1 - rank];
-        if (run + hb >= need) {
-          pick[0] = (uint32_t)(nbins - 1 - rank);
+      bool found = false;
+#pragma unroll
+      for (int i = 0; i < kMaxBpt; ++i) {
+        if (!found && run + cnt[i] >= need) {
+          pick[0] = (uint32_t)(nbins - 1 - (tid * bpt + i));
           pick[1] = run;
-          pick[2] = hb;
-          break;
+          pick[2] = cnt[i];
+          found = true;
         }
-        run += hb;
+        run += cnt[i];
       }
     }
+    // The next write of `pick` comes after two barriers of the next pass.
     __syncthreads();
     const uint32_t digit = pick[0], above = pick[1], cand = pick[2];
-    __syncthreads();
     prefix = (prefix << nb) | digit;
     shift = ns;
     need -= above;
     first = false;
+    hb ^= 1;
     if (cand == need) break;
   }
 
@@ -263,9 +293,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     gtm &= vmask;
     eqm &= vmask;
     uint32_t total;
-    const uint32_t excl =
-        block_exclusive_scan<kTopkWaves>(((uint32_t)__popc(gtm) << 16) | (uint32_t)__popc(eqm), red,
-                                         &total);
+    // Scans of consecutive chunks use different words; each scan's barrier
+    // orders the reads of the one before.
+    const uint32_t excl = block_exclusive_scan<kTopkWaves>(
+        ((uint32_t)__popc(gtm) << 16) | (uint32_t)__popc(eqm), scan_sh[2 + (c & 1)], &total);
     uint32_t g = gt_run + (excl >> 16);
     uint32_t e = eq_run + (excl & 0xFFFFu);
     uint32_t m = gtm | eqm;

@@ -176,6 +176,13 @@ def _topk_case_rows(width, k):
     rows.append(("chunked huge range", (rng.standard_normal(70000) * 1e30).astype(np.float32)))
     rows.append(("denormals", (rng.integers(1, 100, 8000) * np.float32(1e-45)).astype(np.float32)))
     rows.append(("mixed signs", rng.standard_normal(32768).astype(np.float32) * 1e-3))
+    # indexer-like scores: multiples of 0.5 around 2240, a few dozen keys tied
+    # with the threshold digit (resolved by direct ranking)
+    rows.append(("indexer-like", np.maximum(0, np.round(rng.normal(2240, 400, 32768) * 2) / 2)
+                 .astype(np.float32)))
+    # rows at the ranking limits: every key a candidate, with repeated values
+    rows.append(("short ranked", (rng.integers(0, 40, 511) / 4).astype(np.float32)))
+    rows.append(("short ranked mixed signs", rng.standard_normal(300).astype(np.float32)))
     return rows
 
 
