@@ -2,8 +2,9 @@
 
 A step is the whole hot path over one batch: indexer scores -> top-k ->
 GQA sparse attention (split over the k slots) -> log-sum-exp merge: three
-library calls on one stream (attention and merge fused in
-dsa_sparse_attn_merged), or four with --unfused. The default workload is batch 64 decode at
+library calls on one stream when the attention splits fit one workgroup
+(attention and merge fused in dsa_sparse_attn_merged), four otherwise or with
+--unfused. The default workload is batch 64 decode at
 context 32768, page 64, 64 query / 8 KV heads of dim 128, indexer 64 x 128,
 top-k 2048, bf16, synthetic inputs drawn on the device (randomly permuted
 page tables). Inputs are resident in HBM before the timed region; W warm-up
@@ -185,7 +186,7 @@ def main(argv=None):
     ap.add_argument("--splits", type=int, default=0, help="attention splits (0 = default)")
     ap.add_argument("--block-rows", type=int, default=1, help="rows per indexer score block")
     ap.add_argument("--unfused", action="store_true",
-                    help="attention and merge as two launches (dsa_sparse_attn + dsa_merge)")
+                    help="always run attention and merge as two launches (dsa_sparse_attn + dsa_merge)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="oracle time budget for cpu_baseline (0 = skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -221,7 +222,7 @@ def main(argv=None):
     print(f"[bench] generating {wl.name} on the device", file=sys.stderr, flush=True)
     inp = I.generate(wl, "cuda")
     step = DsaStep(inp, num_splits=args.splits or None, block_rows=args.block_rows,
-                   fused=not args.unfused)
+                   fused=False if args.unfused else None)
     torch.cuda.synchronize()
     print(f"[bench] rows {step.rows} width {step.width} splits {step.num_splits}",
           file=sys.stderr, flush=True)

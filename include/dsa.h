@@ -249,7 +249,9 @@ int dsa_sparse_attn_merged_splits(int rows, int num_q_heads, int num_kv_heads, i
  *   M = max_s lse_s,  W = sum_s exp(lse_s - M),
  *   out[r][h] = sum_s exp(lse_s - M) o_s / W,  out_lse[r][h] = M + ln W
  *
- * and out = 0, out_lse = -inf when every split is empty.
+ * and out = 0, out_lse = -inf when every split is empty. Up to 8 splits are
+ * summed in split order (the order dsa_sparse_attn_merged uses); more splits
+ * are summed as four interleaved partial merges, rescaled and added.
  *
  *   part_o, part_lse  device, as written by dsa_sparse_attn
  *   out      device [rows][num_q_heads][head_dim] out_dtype (bf16 rounds to

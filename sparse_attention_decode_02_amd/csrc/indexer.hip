@@ -262,7 +262,8 @@ int indexer_chunk_keys(int num_blocks, int width, int num_heads, int head_dim) {
   const int max_chunk = per_block > 1 ? 1024 : 2048;
   int chunk = (width + per_block - 1) / per_block;
   chunk = ((chunk + 63) / 64) * 64;
-  return max(64, min(max_chunk, chunk));
+  // At least 256 keys (four tiles per wave) to amortize the query load.
+  return max(256, min(max_chunk, chunk));
 }
 
 hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kcache,

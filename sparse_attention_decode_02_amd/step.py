@@ -19,10 +19,13 @@ class DsaStep:
     """Buffers and launches for one step of ``inp`` (a StepInputs on a CUDA
     device). ``block_rows`` > 1 groups consecutive rows of a request into
     score blocks for the indexer. ``fused`` runs attention and the merge as
-    one launch (dsa_sparse_attn_merged) instead of two."""
+    one launch (dsa_sparse_attn_merged) instead of two; None picks the fused
+    launch whenever its workgroup of splits can hold the split count the
+    library suggests (<= 8 splits, a power of two), and the two launches for
+    small batches that want many splits."""
 
     def __init__(self, inp, num_splits: int | None = None, block_rows: int = 1,
-                 fused: bool = False):
+                 fused: bool | None = False):
         wl = inp.wl
         dev = inp.q.device
         self.inp = inp
@@ -36,10 +39,13 @@ class DsaStep:
         self.blocks = None
         if block_rows > 1:
             self.blocks = torch.from_numpy(lib.plan_blocks(req, block_rows)).to(dev)
+        shape = (self.rows, wl.hq, wl.hkv, wl.d, wl.topk, inp.q.dtype)
+        if fused is None:
+            s = num_splits or lib.sparse_attn_splits(*shape)
+            fused = s <= 8 and (s & (s - 1)) == 0
         self.fused = fused
         splits_of = lib.sparse_attn_merged_splits if fused else lib.sparse_attn_splits
-        self.num_splits = num_splits or splits_of(self.rows, wl.hq, wl.hkv, wl.d, wl.topk,
-                                                  inp.q.dtype)
+        self.num_splits = num_splits or splits_of(*shape)
         self.scores = torch.empty(self.rows, self.width, dtype=torch.float32, device=dev)
         self.idx = torch.empty(self.rows, wl.topk, dtype=torch.int32, device=dev)
         parts = 0 if fused else self.rows

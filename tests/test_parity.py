@@ -256,7 +256,7 @@ def test_determinism():
 def _full(wl, rows_fn):
     _say(f"{wl.name}: generating on the device")
     inp = I.generate(wl, "cuda")
-    step = run_step(inp, fused=True)  # the launch configuration bench.py times
+    step = run_step(inp, fused=None)  # the launch configuration bench.py times
     _say(f"  rows {step.rows}, width {step.width}, splits {step.num_splits}")
     check_properties(step)
     rows = rows_fn(step)
