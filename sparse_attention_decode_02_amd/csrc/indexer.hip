@@ -36,6 +36,7 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 constexpr int kIdxThreads = 256;  // 4 waves
 constexpr int kTileKeys = 16;     // keys per MFMA tile (N of 16x16x32)
 constexpr int kKeyBufs = 3;       // key tiles per wave: 2 in flight + 1 on the matrix cores
+constexpr int kMaxChunkKeys = 2048;  // keys per workgroup chunk, at most (scores staged in LDS)
 
 // max(x, 0) as a signed-integer max of the bits: one VALU op, -0.0 -> +0.0.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
@@ -66,6 +67,7 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_mfma_kernel(
   constexpr int QST = DI + 8;  // padded LDS row (elements): the 16 rows read together hit distinct banks
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[H * QST];
   __shared__ __attribute__((aligned(16))) float w_lds[H];
+  __shared__ __attribute__((aligned(16))) float s_lds[kMaxChunkKeys];  // the chunk's scores
 
   const int item = xcd_contiguous(blockIdx.x, total);
   const int b = item / chunks;
@@ -162,7 +164,7 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_mfma_kernel(
       }
       part = sum_rows(part);
       const int s = base + kl;
-      if (grp == 0 && s < L) out[s] = part + 0.0f;
+      if (grp == 0 && s < L) s_lds[s - chunk0] = part + 0.0f;
     };
 
     // kKeyBufs key-fragment buffers in rotation: while one tile runs on the
@@ -174,6 +176,20 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_mfma_kernel(
         const int cur = base0 + (it + u) * kStep;
         load_tile(cur + (kKeyBufs - 1) * kStep, kbuf[(u + kKeyBufs - 1) % kKeyBufs]);
         if (it + u < ntiles) score_tile(cur, kbuf[u]);
+      }
+    }
+    // The chunk's scores leave in whole lines with streaming stores once the
+    // chunk is done: writing each tile's 16 scores as they come costs a few
+    // percent of the kernel's time against the key reads.
+    __syncthreads();
+    typedef float f32x4v __attribute__((ext_vector_type(4)));
+    const int nk = end - chunk0;
+    for (int i = tid * 4; i < nk; i += kIdxThreads * 4) {
+      if (i + 4 <= nk) {
+        __builtin_nontemporal_store(*reinterpret_cast<const f32x4v*>(&s_lds[i]),
+                                    reinterpret_cast<f32x4v*>(out + chunk0 + i));
+      } else {
+        for (int j = i; j < nk; ++j) out[chunk0 + j] = s_lds[j];
       }
     }
   }
@@ -259,7 +275,7 @@ int indexer_chunk_keys(int num_blocks, int width, int num_heads, int head_dim) {
   int cap = kern ? device_capacity(kern, kIdxThreads) : 0;
   if (cap <= 0) cap = 1024;
   const int per_block = max(1, cap / max(1, num_blocks));
-  const int max_chunk = per_block > 1 ? 1024 : 2048;
+  const int max_chunk = per_block > 1 ? 1024 : kMaxChunkKeys;
   int chunk = (width + per_block - 1) / per_block;
   chunk = ((chunk + 63) / 64) * 64;
   // At least 256 keys (four tiles per wave) to amortize the query load.
