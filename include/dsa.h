@@ -226,8 +226,9 @@ int dsa_sparse_attn_splits(int rows, int num_q_heads, int num_kv_heads, int head
  *            nearest even) (output)
  *   out_lse  device [rows][num_q_heads] float32 (output), or NULL
  *
- * Supported: as dsa_sparse_attn, with num_splits in {1, 2, 4, 8} and
- * num_splits <= k; out 16-byte aligned.
+ * Supported: as dsa_sparse_attn, with num_splits in {1, 2, 4, 6, 8} and
+ * num_splits <= k; out 16-byte aligned. (Six splits run two pairs of six
+ * waves per workgroup; the result does not depend on it.)
  * ------------------------------------------------------------------------ */
 int dsa_sparse_attn_merged(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_table, const int32_t* row_req, const int32_t* idx,
@@ -235,9 +236,10 @@ int dsa_sparse_attn_merged(const void* q, const void* k_cache, const void* v_cac
                            int page_size, int max_pages, float scale, int num_splits, void* out,
                            float* out_lse, dsa_dtype dtype, void* stream);
 
-/* dsa_sparse_attn_merged_splits: dsa_sparse_attn_splits rounded down to a
- * num_splits dsa_sparse_attn_merged supports (1, 2, 4 or 8). Errors as for
- * dsa_sparse_attn_splits. */
+/* dsa_sparse_attn_merged_splits: a num_splits for dsa_sparse_attn_merged
+ * with these shapes on the current device: 6 when rows x KV groups x 6 waves
+ * fill the device in about one round, else dsa_sparse_attn_splits rounded
+ * down to 1, 2, 4 or 8. Errors as for dsa_sparse_attn_splits. */
 int dsa_sparse_attn_merged_splits(int rows, int num_q_heads, int num_kv_heads, int head_dim,
                                   int k, dsa_dtype dtype, int* num_splits);
 

@@ -194,7 +194,8 @@ int dsa_sparse_attn_merged(const void* q, const void* k_cache, const void* v_cac
   if (ps < 0) return DSA_ERR_SHAPE;
   const int G = num_q_heads / num_kv_heads;
   if (!(head_dim == 64 || head_dim == 128) || !(G == 1 || G == 2 || G == 4 || G == 8 || G == 16) ||
-      !(num_splits == 1 || num_splits == 2 || num_splits == 4 || num_splits == 8))
+      !(num_splits == 1 || num_splits == 2 || num_splits == 4 || num_splits == 6 ||
+        num_splits == 8))
     return DSA_ERR_UNSUPPORTED;
   if (dtype != DSA_BF16 && dtype != DSA_F32) return DSA_ERR_UNSUPPORTED;
   if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 16) ||

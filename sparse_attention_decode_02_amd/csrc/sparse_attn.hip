@@ -135,36 +135,45 @@ template <> struct Elem<float, 1> {
 };
 
 // FS == 0: one wave per workgroup and split, partials written to HBM.
-// FS > 0: the FS splits of one (row, KV group) are the FS waves of one
-// workgroup, merged through LDS into the final output (see the end).
-template <typename T, int D, int G, int FS>
-__global__ __launch_bounds__(64 * (FS > 0 ? FS : 1), (sizeof(T) == 2 && D * G <= 1024) ? 3 : 2) void sparse_attn_kernel(
+// FS > 0: the FS splits of one (row, KV group) are FS waves of one workgroup
+// and are merged through LDS into the final output (see the end); a
+// workgroup holds PP such pairs (PP * FS waves), so that its waves can fill
+// a CU's wave slots exactly (a workgroup's waves are all placed on one CU).
+template <typename T, int D, int G, int FS, int PP = 1>
+__global__ __launch_bounds__(64 * (FS > 0 ? FS * PP : 1), (sizeof(T) == 2 && D * G <= 1024) ? 3 : 2) void sparse_attn_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ row_req,
     const int32_t* __restrict__ idx, int hkv, int k, int page_shift, int max_pages,
     float scale_log2, int S, int chunk, float* __restrict__ part_o,
-    float* __restrict__ part_lse, void* __restrict__ out, float* __restrict__ out_lse) {
+    float* __restrict__ part_lse, void* __restrict__ out, float* __restrict__ out_lse,
+    int npairs) {
   constexpr bool kBf16 = sizeof(T) == 2;
   constexpr int RW = D * (int)sizeof(T) / 4;  // 32-bit words per row
   constexpr int NV4 = RW / 8;                 // uint4 per half row
   constexpr int DPL = D / 64;                 // output dims per lane
-  constexpr int NW = FS > 0 ? FS : 1;         // waves per workgroup
+  constexpr int NW = FS > 0 ? FS * PP : 1;    // waves per workgroup
   typedef Elem<T, DPL> E;
   typedef typename E::Word Word;
-  __shared__ uint4 q_lds[G * RW / 4];
+  __shared__ uint4 q_lds_all[PP][G * RW / 4];
   __shared__ float p_lds_all[NW][kTile * G];
   __shared__ uint32_t rows_lds_all[NW][kSpan];
 
   const int lane = threadIdx.x & 63;
   const int wave = threadIdx.x >> 6;
   const int tl = lane & 31, hf = lane >> 5;
-  const int g = (FS > 0 ? blockIdx.x : blockIdx.x / S) % hkv;
-  const int r = (FS > 0 ? blockIdx.x : blockIdx.x / S) / hkv;
-  const int s = FS > 0 ? wave : (int)(blockIdx.x % S);
+  // (row, KV group) pair of this wave; a workgroup's last pairs may not exist
+  // (their waves skip the work but still meet the workgroup barriers).
+  const int pw = FS > 0 ? wave / FS : 0;  // pair within the workgroup
+  const int pair = FS > 0 ? (int)blockIdx.x * PP + pw : (int)(blockIdx.x / S);
+  const bool live = FS == 0 || pair < npairs;
+  const int g = (live ? pair : 0) % hkv;
+  const int r = (live ? pair : 0) / hkv;
+  const int s = FS > 0 ? wave - pw * FS : (int)(blockIdx.x % S);
+  const uint4* q_lds = q_lds_all[pw];
   float* p_lds = p_lds_all[wave];
   uint32_t* rows_lds = rows_lds_all[wave];
   const int hq = hkv * G;
-  const int a = min(k, s * chunk);
+  const int a = live ? min(k, s * chunk) : k;  // a dead pair's waves get an empty range
   const int b = min(k, a + chunk);
   const int page_mask = (1 << page_shift) - 1;
   const int32_t* btr = bt + (size_t)row_req[r] * max_pages;
@@ -173,9 +182,11 @@ __global__ __launch_bounds__(64 * (FS > 0 ? FS : 1), (sizeof(T) == 2 && D * G <=
   const T* kgroup = kc + (size_t)g * D;
   const T* vgroup = vc + (size_t)g * D;
 
-  {
+  if (live) {
+    // The FS waves of a pair load its query block together.
     const uint4* qsrc = reinterpret_cast<const uint4*>(q + ((size_t)r * hq + (size_t)g * G) * D);
-    for (int i = threadIdx.x; i < G * RW / 4; i += 64 * NW) q_lds[i] = qsrc[i];
+    const int pt = threadIdx.x - pw * FS * 64;  // thread index within the pair
+    for (int i = pt; i < G * RW / 4; i += 64 * (FS > 0 ? FS : 1)) q_lds_all[pw][i] = qsrc[i];
   }
   __syncthreads();  // every wave of the workgroup reads the whole query block
 
@@ -332,8 +343,8 @@ __global__ __launch_bounds__(64 * (FS > 0 ? FS : 1), (sizeof(T) == 2 && D * G <=
     // The FS split partials go to LDS (the same values the unfused kernel
     // writes to HBM) and are merged exactly as dsa_merge does -- same
     // operations in the same split order -- so both paths agree bit for bit.
-    __shared__ float o_lds[FS][G][D];
-    __shared__ float lse_lds[FS][G];
+    __shared__ float o_lds[NW][G][D];
+    __shared__ float lse_lds[NW][G];
 #pragma unroll
     for (int h = 0; h < G; ++h) {
       const float l = wave_sum(lsum[h]);
@@ -344,19 +355,25 @@ __global__ __launch_bounds__(64 * (FS > 0 ? FS : 1), (sizeof(T) == 2 && D * G <=
       if (lane == 0) lse_lds[wave][h] = any ? (m[h] + __log2f(l)) * kLn2 : -INFINITY;
     }
     __syncthreads();
-    for (int i = threadIdx.x; i < G * D; i += 64 * FS) {
-      const int h = i / D, e = i - h * D;
+    for (int i = threadIdx.x; i < PP * G * D; i += 64 * NW) {
+      const int pp = i / (G * D);
+      const int hd = i - pp * G * D;
+      const int h = hd / D, e = hd - h * D;
+      const int pr = (int)blockIdx.x * PP + pp;
+      if (pr >= npairs) break;  // the pairs past the end come last
+      const int r = pr / hkv, g = pr - r * hkv;
+      const int w0 = pp * FS;
       float M = -INFINITY;
 #pragma unroll
-      for (int u = 0; u < FS; ++u) M = fmaxf(M, lse_lds[u][h]);
+      for (int u = 0; u < FS; ++u) M = fmaxf(M, lse_lds[w0 + u][h]);
       const bool any = M != -INFINITY;
       const float Mr = any ? M : 0.0f;
       float W = 0.0f, acc = 0.0f;
 #pragma unroll
       for (int u = 0; u < FS; ++u) {
-        const float wgt = __expf(lse_lds[u][h] - Mr);
+        const float wgt = __expf(lse_lds[w0 + u][h] - Mr);
         W += wgt;
-        acc = fmaf(wgt, o_lds[u][h][e], acc);
+        acc = fmaf(wgt, o_lds[w0 + u][h][e], acc);
       }
       const float invW = any ? 1.0f / W : 0.0f;
       const float x = acc * invW;
@@ -368,7 +385,7 @@ __global__ __launch_bounds__(64 * (FS > 0 ? FS : 1), (sizeof(T) == 2 && D * G <=
   }
 }
 
-template <typename T, int FS>
+template <typename T, int FS, int PP = 1>
 static hipError_t launch_attn_t(const T* q, const T* kc, const T* vc, const int32_t* bt,
                                 const int32_t* row_req, const int32_t* idx, int rows, int hq,
                                 int hkv, int d, int k, int page_shift, int max_pages, float scale,
@@ -376,13 +393,14 @@ static hipError_t launch_attn_t(const T* q, const T* kc, const T* vc, const int3
                                 hipStream_t stream) {
   const int G = hq / hkv;
   const int chunk = (k + S - 1) / S;
-  const dim3 grid(FS > 0 ? (unsigned)rows * hkv : (unsigned)rows * S * hkv);
-  const dim3 block(64 * (FS > 0 ? FS : 1));
+  const int npairs = rows * hkv;
+  const dim3 grid(FS > 0 ? (unsigned)((npairs + PP - 1) / PP) : (unsigned)rows * S * hkv);
+  const dim3 block(64 * (FS > 0 ? FS * PP : 1));
   const float sl2 = scale * kLog2e;
 #define DSA_ATTN(D_, G_)                                                                        \
-  hipLaunchKernelGGL((sparse_attn_kernel<T, D_, G_, FS>), grid, block, 0, stream, q, kc, vc, bt, \
-                     row_req, idx, hkv, k, page_shift, max_pages, sl2, S, chunk, part_o,         \
-                     part_lse, out, out_lse)
+  hipLaunchKernelGGL((sparse_attn_kernel<T, D_, G_, FS, PP>), grid, block, 0, stream, q, kc, vc, \
+                     bt, row_req, idx, hkv, k, page_shift, max_pages, sl2, S, chunk, part_o,      \
+                     part_lse, out, out_lse, npairs)
 #define DSA_ATTN_G(D_)                    \
   switch (G) {                            \
     case 1: DSA_ATTN(D_, 1); break;       \
@@ -453,14 +471,21 @@ static hipError_t launch_merged_t(const void* q, const void* kc, const void* vc,
   const T* q_ = static_cast<const T*>(q);
   const T* k_ = static_cast<const T*>(kc);
   const T* v_ = static_cast<const T*>(vc);
-#define DSA_MERGED(FS_)                                                                         \
-  return launch_attn_t<T, FS_>(q_, k_, v_, bt, row_req, idx, rows, hq, hkv, d, k, page_shift,   \
-                               max_pages, scale, S, nullptr, nullptr, out, out_lse, stream)
+#define DSA_MERGED(FS_, PP_)                                                                   \
+  return launch_attn_t<T, FS_, PP_>(q_, k_, v_, bt, row_req, idx, rows, hq, hkv, d, k,          \
+                                    page_shift, max_pages, scale, S, nullptr, nullptr, out,     \
+                                    out_lse, stream)
+  // Six splits run as two (row, KV group) pairs per workgroup: twelve waves
+  // fill a CU's wave slots at three waves per SIMD, where a six-wave
+  // workgroup would leave half of them empty.
+  // (fp32 rows keep one pair per workgroup: two would exceed the LDS.)
+  constexpr int kPairs6 = sizeof(T) == 2 ? 2 : 1;
   switch (S) {
-    case 1: DSA_MERGED(1);
-    case 2: DSA_MERGED(2);
-    case 4: DSA_MERGED(4);
-    case 8: DSA_MERGED(8);
+    case 1: DSA_MERGED(1, 1);
+    case 2: DSA_MERGED(2, 1);
+    case 4: DSA_MERGED(4, 1);
+    case 6: DSA_MERGED(6, kPairs6);
+    case 8: DSA_MERGED(8, 1);
     default: return hipErrorInvalidValue;
   }
 #undef DSA_MERGED
@@ -479,8 +504,22 @@ hipError_t launch_sparse_attn_merged(const void* q, const void* kc, const void* 
 }
 
 int merged_default_splits(int rows, int hq, int hkv, int d, int k, bool bf16) {
-  // The fused kernel runs the same waves as the split kernel; round the split
-  // count to a supported workgroup size (1, 2, 4 or 8 waves).
+  // Six splits in workgroups of two pairs when that fills the device in one
+  // round at three waves per SIMD (the rows x KV groups are many, the
+  // occupancy allows it); otherwise the split kernel's suggestion rounded
+  // down to a supported workgroup size (1, 2, 4 or 8 waves).
+  const void* kern = bf16 ? attn_kernel_ptr<uint16_t>(d, hq / hkv) : attn_kernel_ptr<float>(d, hq / hkv);
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 0;
+  int cap = kern ? device_capacity(kern, 64) : 0;
+  if (cap <= 0 || cus <= 0) {
+    cus = 256;
+    cap = 3072;
+  }
+  const long long pairs = (long long)rows * hkv;
+  if (cap / cus == 12 && k >= 6 * 32 && pairs * 6 <= cap && pairs * 6 * 2 >= cap) return 6;
   const int s = attn_default_splits(rows, hq, hkv, d, k, bf16);
   int f = 1;
   while (f * 2 <= s && f * 2 <= 8 && f * 2 <= k) f *= 2;

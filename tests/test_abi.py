@@ -209,7 +209,7 @@ def test_attn_splits_rejects(args, code):
     (dict(q=None), NULL), (dict(out=None), NULL), (dict(idx=None), NULL),
     (dict(rows=-1), SHAPE), (dict(hkv=3), SHAPE), (dict(num_splits=0), SHAPE),
     (dict(k=2, num_splits=4), SHAPE), (dict(scale=float("nan")), SHAPE),
-    (dict(num_splits=3), UNSUP), (dict(num_splits=16), UNSUP), (dict(d=96), UNSUP),
+    (dict(num_splits=3), UNSUP), (dict(num_splits=5), UNSUP), (dict(num_splits=16), UNSUP), (dict(d=96), UNSUP),
     (dict(out=A + 2), ALIGN), (dict(out_lse=A + 2), ALIGN), (dict(q=A + 4), ALIGN),
     (dict(rows=0), OK),
 ])

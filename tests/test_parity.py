@@ -91,7 +91,7 @@ def test_split_counts(S):
         check_row(step, r)
 
 
-@pytest.mark.parametrize("S", [1, 2, 4, 8])
+@pytest.mark.parametrize("S", [1, 2, 4, 6, 8])
 def test_merged_matches_split_then_merge_bitwise(S):
     """dsa_sparse_attn_merged writes exactly what dsa_sparse_attn + dsa_merge
     write, and both match the oracle."""
@@ -113,7 +113,7 @@ def test_merged_shapes(v):
     wl = I.custom(I.tiny(), name="variant", dtype=dt, page=page, hq=hq, hkv=hkv, d=d, hi=hi,
                   di=di, topk=topk, prior=(3, 150, 700, 40), new=(1, 1, 1, 6), seed=77)
     inp = _host_inputs(wl)
-    for S in (1, 2, 4):
+    for S in (1, 2, 4, 6):
         two = run_step(inp, num_splits=S)
         one = run_step(inp, num_splits=S, fused=True)
         dtv = torch.int16 if dt == "bf16" else torch.int32
