@@ -8,31 +8,35 @@
 // largest scores, ties to the lower position, and write them in ascending
 // order. L <= k: every position, then -1.
 //
-// One workgroup of 1024 threads per row; a thread owns 32 consecutive
-// positions of each 32768-position chunk, held in registers as order-
-// preserving 32-bit keys (-0.0 canonicalized to +0.0). The threshold key is
-// found by radix select on those keys:
+// One workgroup of 1024 threads per row; a thread owns 32 (or, for batches
+// of few rows wider than 32768, 64) consecutive positions of each chunk, held
+// in registers as order-preserving 32-bit keys (-0.0 canonicalized to +0.0).
+// The threshold key is found by radix select on those keys:
 //   * a min/max reduction skips the bits every key shares, so the first
 //     12-bit digit falls where the row's values actually differ (scores of a
 //     row usually share sign and leading exponent bits, which would otherwise
 //     pile every key into one or two bins);
 //   * each pass histograms the next <= 12 bits of the keys still tied with
-//     the threshold prefix (LDS atomics) and a block scan over the bins, from
+//     the threshold prefix (LDS atomics; two buffers, so the next pass's is
+//     cleared while this one is read) and a block scan over the bins, from
 //     the top, picks the digit holding the k-th largest;
 //   * it stops when the bits run out or every key still tied is needed.
 // The emit pass is an ordered compaction: each thread counts its keys above
 // the threshold prefix and equal to it, one block-wide exclusive scan gives
 // every thread its output offset, and keys equal to the prefix are taken in
 // position order until the remaining need is met -- which is exactly
-// "ties to the lower position". Rows longer than 32768 positions re-read
-// their chunks from cache on every pass.
+// "ties to the lower position". Rows longer than a chunk re-read their
+// chunks from cache on every pass. Wave reductions and scans use DPP row
+// operations and lane reads rather than LDS permutes, and every block scan
+// has its own per-wave words, so a radix pass takes three barriers.
+
+#include <type_traits>
 
 #include "dsa_kernels.h"
 
 namespace dsa {
 
 constexpr int kTopkThreads = 1024;  // threads of the launched configuration
-constexpr int kVPTDefault = 32;      // positions per thread per chunk
 constexpr int kDigitBits = 12;
 constexpr int kBins = 1 << kDigitBits;
 
@@ -41,6 +45,11 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   if (u == 0x80000000u) u = 0u;  // -0.0 ranks as +0.0
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
+
+__device__ __forceinline__ int popcount(uint32_t m) { return __popc(m); }
+__device__ __forceinline__ int popcount(uint64_t m) { return __popcll(m); }
+__device__ __forceinline__ int lowest_bit(uint32_t m) { return __ffs(m) - 1; }
+__device__ __forceinline__ int lowest_bit(uint64_t m) { return __ffsll((unsigned long long)m) - 1; }
 
 __device__ __forceinline__ uint32_t high_bits(uint32_t key, int shift) {
   return shift >= 32 ? 0u : (key >> shift);
@@ -112,6 +121,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   constexpr int kTopkThreads = kThreads;
   constexpr int kTopkWaves = kThreads / 64;
   constexpr int kChunk = kThreads * kVPT;
+  // One bit per position a thread owns in a chunk.
+  typedef typename std::conditional<(kVPT <= 32), uint32_t, uint64_t>::type Mask;
+  static_assert(kVPT <= 64, "a thread's positions must fit one 64-bit mask");
   __shared__ uint32_t hist[2][kBins];  // alternate passes: one fills while the other is cleared
   __shared__ uint32_t scan_sh[4][kTopkWaves];  // per-wave words of the block scans, by use
   __shared__ uint32_t red[2 * kTopkWaves];
@@ -282,30 +294,30 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   for (int c = 0; c < nchunks; ++c) {
     if (!resident) load_chunk(c);
     const int base = c * kChunk + tid * kVPT;
-    uint32_t gtm = 0u, eqm = 0u;
+    Mask gtm = 0, eqm = 0;
 #pragma unroll
     for (int j = 0; j < kVPT; ++j) {
       const uint32_t hb = key[j] >> shift;
-      gtm |= (uint32_t)(hb > prefix) << j;
-      eqm |= (uint32_t)(hb == prefix) << j;
+      gtm |= (Mask)(hb > prefix) << j;
+      eqm |= (Mask)(hb == prefix) << j;
     }
-    const uint32_t vmask = nv == kVPT ? 0xFFFFFFFFu : ((1u << nv) - 1u);
+    const Mask vmask = nv == kVPT ? ~(Mask)0 : (((Mask)1 << nv) - 1);
     gtm &= vmask;
     eqm &= vmask;
     uint32_t total;
     // Scans of consecutive chunks use different words; each scan's barrier
     // orders the reads of the one before.
     const uint32_t excl = block_exclusive_scan<kTopkWaves>(
-        ((uint32_t)__popc(gtm) << 16) | (uint32_t)__popc(eqm), scan_sh[2 + (c & 1)], &total);
+        ((uint32_t)popcount(gtm) << 16) | (uint32_t)popcount(eqm), scan_sh[2 + (c & 1)], &total);
     uint32_t g = gt_run + (excl >> 16);
     uint32_t e = eq_run + (excl & 0xFFFFu);
-    uint32_t m = gtm | eqm;
+    Mask m = gtm | eqm;
     while (m) {
-      const int j = __ffs(m) - 1;
-      m &= m - 1u;
+      const int j = lowest_bit(m);
+      m &= m - 1;
       // Every slot written is < k by construction; the bound keeps a broken
       // invariant from ever turning into an out-of-row store.
-      if ((gtm >> j) & 1u) {
+      if ((gtm >> j) & 1) {
         const uint32_t slot = g + min(e, need);
         if (slot < (uint32_t)k) out[slot] = base + j;
         ++g;
@@ -321,8 +333,21 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
 
 hipError_t launch_topk(const float* scores, const int32_t* row_len, int rows, int width, int k,
                        int32_t* idx, hipStream_t stream) {
-  hipLaunchKernelGGL((topk_kernel<kTopkThreads, kVPTDefault>), dim3(rows), dim3(kTopkThreads), 0,
-                     stream, scores, row_len, width, k, idx);
+  // 32 keys per thread cover rows up to 32768 positions in registers. Wider
+  // batches of few rows (the long rows set the kernel's time) hold 64 keys per
+  // thread, which halves the chunk re-reads of rows past 32768; batches of
+  // many rows fill the device either way and keep 32 (shorter rows then use
+  // more of the workgroup's threads).
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  if (width > kTopkThreads * 32 && rows <= cus)
+    hipLaunchKernelGGL((topk_kernel<kTopkThreads, 64>), dim3(rows), dim3(kTopkThreads), 0, stream,
+                       scores, row_len, width, k, idx);
+  else
+    hipLaunchKernelGGL((topk_kernel<kTopkThreads, 32>), dim3(rows), dim3(kTopkThreads), 0, stream,
+                       scores, row_len, width, k, idx);
   return hipGetLastError();
 }
 

@@ -187,10 +187,13 @@ def _topk_case_rows(width, k):
 
 
 @pytest.mark.parametrize("k", [1, 16, 2048])
-def test_topk_edges(k):
+@pytest.mark.parametrize("copies", [1, 13], ids=["few-rows", "many-rows"])
+def test_topk_edges(k, copies):
+    """Edge rows against the oracle. A batch of few wide rows runs the
+    64-keys-per-thread kernel, a batch of more rows than CUs the 32-keys one."""
     from sparse_attention_decode_02_amd import lib
     width = 70016
-    cases = _topk_case_rows(width, k)
+    cases = _topk_case_rows(width, k) * copies
     _say(f"top-k edges, k {k}, {len(cases)} rows")
     scores = np.full((len(cases), width), np.nan, np.float32)
     lens = np.zeros(len(cases), np.int32)
