@@ -83,14 +83,15 @@ def _events(torch):
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def time_steps(step, steps, warmup, torch):
+def time_steps(step, steps, warmup, torch, graph=None):
+    run = graph.replay if graph is not None else step.run
     for _ in range(warmup):
-        step.run()
+        run()
     torch.cuda.synchronize()
     a, b = _events(torch)
     a.record()
     for _ in range(steps):
-        step.run()
+        run()
     b.record()
     torch.cuda.synchronize()
     return a.elapsed_time(b) / steps  # ms
@@ -187,6 +188,8 @@ def main(argv=None):
     ap.add_argument("--block-rows", type=int, default=1, help="rows per indexer score block")
     ap.add_argument("--unfused", action="store_true",
                     help="always run attention and merge as two launches (dsa_sparse_attn + dsa_merge)")
+    ap.add_argument("--graph", action="store_true",
+                    help="record the step into a HIP graph once and time its replays")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="oracle time budget for cpu_baseline (0 = skip)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -227,7 +230,8 @@ def main(argv=None):
     print(f"[bench] rows {step.rows} width {step.width} splits {step.num_splits}",
           file=sys.stderr, flush=True)
 
-    ms = time_steps(step, args.steps, args.warmup, torch)
+    graph = step.capture() if args.graph else None
+    ms = time_steps(step, args.steps, args.warmup, torch, graph)
     kern = time_kernels(step, args.steps, torch)
     layer_us = ms * 1000.0
     ab = algorithmic_bytes(wl, step.row_len_host)
@@ -266,6 +270,7 @@ def main(argv=None):
             "attention_splits": step.num_splits,
             "indexer_block_rows": args.block_rows,
             "attention_merge": "fused" if step.fused else "separate",
+            "launch": "graph replay" if args.graph else "stream",
         },
         "hbm_gbps": round(gbps, 1),
         "layer_frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),

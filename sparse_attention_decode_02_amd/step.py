@@ -1,6 +1,7 @@
 """One paged DSA step on the GPU: the row plan, the buffers between the stages,
 and the library calls in order on one stream (four, or three with the
-attention and merge fused).
+attention and merge fused), optionally recorded once into a HIP graph and
+replayed.
 
 torch supplies only the device memory and the stream; the row plan comes
 from the library's host entry points and every stage runs in its kernels.
@@ -87,3 +88,23 @@ class DsaStep:
         self.attention(stream)
         self.merge(stream)
         return self.out
+
+    def capture(self):
+        """Records the step's launches into a HIP graph (torch's graph capture
+        on ROCm) and returns it; ``graph.replay()`` runs them again on the same
+        buffers. The kernels read the metadata (lengths, request ids, block
+        tables, selected positions) from device memory when they run, so those
+        may change between replays as long as the score width and row count
+        stay the same. Nothing the step records clears memory with a memset
+        node: every output is written by a kernel."""
+        import torch
+
+        graph = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            self.run()  # one eager pass on the capturing side before recording
+        torch.cuda.current_stream().wait_stream(side)
+        with torch.cuda.graph(graph):
+            self.run()
+        return graph

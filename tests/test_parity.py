@@ -17,6 +17,7 @@ import torch
 from dsa_check import CANARY, check_properties, check_row, oracle_row, run_step
 from oracle import dsa_oracle as O
 from sparse_attention_decode_02_amd import inputs as I
+from sparse_attention_decode_02_amd.step import DsaStep
 
 pytestmark = pytest.mark.gpu
 
@@ -240,6 +241,61 @@ def test_score_blocks_are_bit_identical():
     for br in (2, 5, 16, 64):
         s = run_step(inp, block_rows=br).scores
         assert torch.equal(s.view(torch.int32), ref.view(torch.int32)), f"block_rows {br}"
+
+
+@pytest.mark.parametrize("fused", [True, False], ids=["fused", "two-launch"])
+def test_graph_replay_matches_eager(fused):
+    """The step recorded into a HIP graph and replayed gives the eager step's
+    bits on every replay, with eager work in between, and follows row lengths
+    changed in device memory between replays (same width)."""
+    _say(f"graph replay, fused {fused}")
+    inp = _host_inputs(_small_mixed(seed=17))
+    step = DsaStep(inp, num_splits=4, fused=fused)
+    outs = lambda: [t.clone() for t in (step.scores, step.idx, step.out, step.out_lse)]
+
+    def same(a, b):
+        # scores past a row's length are not written: compare the written part
+        la = step.row_len.cpu().numpy()
+        for r in range(step.rows):
+            assert torch.equal(a[0][r, : la[r]].view(torch.int32), b[0][r, : la[r]].view(torch.int32)), r
+        for x, y in zip(a[1:], b[1:]):
+            assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+
+    def clear():
+        step.scores.view(torch.int32).fill_(CANARY)
+        for t in (step.idx, step.out, step.out_lse):
+            t.zero_()
+
+    clear()
+    step.run()
+    torch.cuda.synchronize()
+    eager = outs()
+    graph = step.capture()
+    torch.cuda.synchronize()
+    other = DsaStep(_host_inputs(_small_mixed(seed=18)), num_splits=2)
+    for rep in range(3):
+        clear()
+        graph.replay()
+        torch.cuda.synchronize()
+        same(outs(), eager)
+        other.run()  # eager work between replays
+        torch.cuda.synchronize()
+    # shorter rows in place, then eager and replayed results must agree
+    new_len = step.row_len.clone()
+    new_len[::3] = torch.clamp(new_len[::3] - 37, min=0)
+    step.row_len.copy_(new_len)
+    clear()
+    step.run()
+    torch.cuda.synchronize()
+    eager2 = outs()
+    for rep in range(2):
+        clear()
+        graph.replay()
+        torch.cuda.synchronize()
+        same(outs(), eager2)
+    step.row_len_host = new_len.cpu().numpy()
+    for r in (0, 3, 36, step.rows - 1):
+        check_row(step, r)
 
 
 def test_determinism():
