@@ -159,7 +159,9 @@ __global__ __launch_bounds__(64 * (FS > 0 ? FS * PP : 1), (sizeof(T) == 2 && D *
   __shared__ uint32_t rows_lds_all[NW][kSpan];
 
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
+  // Uniform across the wave: everything derived from it (the pair, the
+  // split, LDS slots, cache and index pointers) stays in scalar registers.
+  const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
   const int tl = lane & 31, hf = lane >> 5;
   // (row, KV group) pair of this wave; a workgroup's last pairs may not exist
   // (their waves skip the work but still meet the workgroup barriers).
