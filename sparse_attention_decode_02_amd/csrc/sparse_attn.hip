@@ -227,7 +227,7 @@ __global__ __launch_bounds__(64 * (FS > 0 ? FS * PP : 1), (sizeof(T) == 2 && D *
       if (i < n) rows_lds[i] = row;
       if (pos[u] >= 0) last = i;
     }
-    last = wave_max_i32(last);
+    last = __builtin_amdgcn_readfirstlane(wave_max_i32(last));  // uniform: a scalar loop bound
     wave_sync();
     const int ntiles = (last + kTile) / kTile;  // tiles up to the last selected slot
 
