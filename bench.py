@@ -183,11 +183,17 @@ def main(argv=None):
     ap.add_argument("--steps", type=int, default=50)
     ap.add_argument("--warmup", type=int, default=10)
     ap.add_argument("--workload", default="headline",
-                    help="headline (default), decode, tiny, ragged or mixed")
+                    help="headline (default), decode, tiny, ragged, mixed or long")
     ap.add_argument("--splits", type=int, default=0, help="attention splits (0 = default)")
     ap.add_argument("--block-rows", type=int, default=1, help="rows per indexer score block")
     ap.add_argument("--unfused", action="store_true",
                     help="always run attention and merge as two launches (dsa_sparse_attn + dsa_merge)")
+    ap.add_argument("--topk-chunk", type=int, default=-1,
+                    help="top-k segment length for the two-stage selection (0 = one pass, "
+                         "-1 = the library's suggestion)")
+    ap.add_argument("--score-buffer-mib", type=int, default=0,
+                    help="score and select in row windows through a buffer of this many MiB "
+                         "(0 = every row at once)")
     ap.add_argument("--graph", action="store_true",
                     help="record the step into a HIP graph once and time its replays")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
@@ -225,7 +231,9 @@ def main(argv=None):
     print(f"[bench] generating {wl.name} on the device", file=sys.stderr, flush=True)
     inp = I.generate(wl, "cuda")
     step = DsaStep(inp, num_splits=args.splits or None, block_rows=args.block_rows,
-                   fused=False if args.unfused else None)
+                   fused=False if args.unfused else None,
+                   topk_chunk=None if args.topk_chunk < 0 else args.topk_chunk,
+                   score_buffer_bytes=(args.score_buffer_mib << 20) if args.score_buffer_mib else None)
     torch.cuda.synchronize()
     print(f"[bench] rows {step.rows} width {step.width} splits {step.num_splits}",
           file=sys.stderr, flush=True)
@@ -271,6 +279,9 @@ def main(argv=None):
             "indexer_block_rows": args.block_rows,
             "attention_merge": "fused" if step.fused else "separate",
             "launch": "graph replay" if args.graph else "stream",
+            "topk": (f"two-stage, {step.topk_chunk}-position segments" if step.topk_chunk
+                     else "one pass"),
+            "score_rows_per_window": step.window_rows,
         },
         "hbm_gbps": round(gbps, 1),
         "layer_frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),

@@ -55,7 +55,7 @@ typedef enum {
   DSA_ERR_SHAPE = -2,       /* a size is out of range or inconsistent */
   DSA_ERR_ALIGN = -3,       /* a device pointer is not 16-byte aligned */
   DSA_ERR_UNSUPPORTED = -4, /* head count / head dim / dtype combination not built */
-  DSA_ERR_WORKSPACE = -5,   /* reserved */
+  DSA_ERR_WORKSPACE = -5,   /* a workspace buffer is too small */
   DSA_ERR_LAUNCH = -6       /* the kernel launch failed */
 } dsa_status;
 
@@ -162,6 +162,72 @@ int dsa_indexer_scores(const void* q_idx, const float* w, const void* k_idx_cach
  * ------------------------------------------------------------------------ */
 int dsa_topk(const float* scores, const int32_t* row_len, int rows, int width, int k,
              int32_t* idx, void* stream);
+
+/* ------------------------------------------------------------------------
+ * dsa_topk_chunked -- the same selection as dsa_topk, in two stages.
+ *
+ * Commit "Replace handwritten inline PTX selection with a CuTe DSL histogram
+ * fast path ..." keeps exact chunk merging for long contexts. Stage 1 takes
+ * the exact top-k of every segment [c*chunk, (c+1)*chunk) of every row (one
+ * workgroup per segment, so a long row spreads over many compute units);
+ * stage 2 takes each row's exact top-k among its segments' winners. Every
+ * position of the row's top-k is among its segment's top-k, so the result is
+ * dsa_topk's, bit for bit: same positions, same order, same -1 padding.
+ *
+ *   scores   device [rows][width] float32, 16-byte aligned
+ *   row_len  device [rows] int32
+ *   cand     device int32 workspace of cand_slots entries, at least
+ *            rows * ceil(width / chunk) * k (dsa_topk_chunked_slots);
+ *            overwritten, holds no result
+ *   idx      device [rows][k] int32 (output)
+ *
+ * k <= chunk <= 2^20, chunk a multiple of 4; 1 <= k <= width; width a
+ * positive multiple of 4. cand_slots too small: DSA_ERR_WORKSPACE.
+ * ------------------------------------------------------------------------ */
+int dsa_topk_chunked(const float* scores, const int32_t* row_len, int rows, int width, int k,
+                     int chunk, int32_t* cand, long long cand_slots, int32_t* idx, void* stream);
+
+/* Candidate slots dsa_topk_chunked needs for these sizes (host). */
+int dsa_topk_chunked_slots(int rows, int width, int k, int chunk, long long* slots);
+
+/* The segment length at which dsa_topk_chunked is expected to beat dsa_topk
+ * on the current device for these sizes (rows longer than one workgroup holds
+ * in registers, few enough segments to run at once), or 0 (host). */
+int dsa_topk_chunk_suggest(int rows, int width, int k, int* chunk);
+
+/* ------------------------------------------------------------------------
+ * dsa_indexer_topk_windowed -- indexer scores and top-k in row windows.
+ *
+ * Commit "Score and select rows in windows whose score buffer fits ...": the
+ * rows are scored and selected a window at a time through one caller-given
+ * score buffer, so its size bounds the score memory at any context length.
+ * A window holds window_rows = score_buffer_bytes / (width * 4) rows
+ * (dsa_select_window_rows); the window count depends only on rows and width,
+ * so the launch sequence is the same for every step of those sizes. Each
+ * window runs dsa_indexer_scores on rows [r0, r0 + n) into the buffer, then
+ * dsa_topk (topk_chunk == 0) or dsa_topk_chunked (topk_chunk > 0, with cand
+ * sized for one window) into idx rows [r0, r0 + n). Results equal those of
+ * dsa_indexer_scores over all rows followed by the same selection.
+ *
+ *   q_idx, w, k_idx_cache, block_table, row_req, row_len: as for
+ *            dsa_indexer_scores (all rows; no score blocks)
+ *   score_buffer  device float32 workspace of score_buffer_bytes, 16-byte
+ *            aligned; overwritten, holds no result
+ *   cand, cand_slots  as for dsa_topk_chunked, for window_rows rows (unused,
+ *            may be NULL, when topk_chunk == 0)
+ *   idx      device [rows][k] int32 (output)
+ *
+ * A buffer smaller than one score row: DSA_ERR_WORKSPACE.
+ * ------------------------------------------------------------------------ */
+int dsa_indexer_topk_windowed(const void* q_idx, const float* w, const void* k_idx_cache,
+                              const int32_t* block_table, const int32_t* row_req,
+                              const int32_t* row_len, int rows, int width, int num_heads,
+                              int head_dim, int page_size, int max_pages, dsa_dtype dtype, int k,
+                              float* score_buffer, long long score_buffer_bytes, int topk_chunk,
+                              int32_t* cand, long long cand_slots, int32_t* idx, void* stream);
+
+/* Rows per window for a score buffer of score_buffer_bytes (host). */
+int dsa_select_window_rows(int width, long long score_buffer_bytes, int* window_rows);
 
 /* ------------------------------------------------------------------------
  * dsa_sparse_attn -- GQA sparse attention over split k-slot slices.

@@ -97,21 +97,22 @@ int dsa_score_width(int rows, const int32_t* row_len, int* width) {
   return DSA_OK;
 }
 
-int dsa_indexer_scores(const void* q_idx, const float* w, const void* k_idx_cache,
-                       const int32_t* block_table, const int32_t* row_req, const int32_t* row_len,
-                       const int32_t* blocks, int num_blocks, float* scores, int rows, int width,
-                       int num_heads, int head_dim, int page_size, int max_pages, dsa_dtype dtype,
-                       void* stream) {
+}  // extern "C"
+
+namespace {
+
+// Argument checks of dsa_indexer_scores; *page_shift gets log2(page_size).
+int indexer_check(const void* q_idx, const float* w, const void* k_idx_cache,
+                  const int32_t* block_table, const int32_t* row_req, const int32_t* row_len,
+                  const int32_t* blocks, int num_blocks, const float* scores, int rows, int width,
+                  int num_heads, int head_dim, int page_size, int max_pages, dsa_dtype dtype,
+                  int* page_shift) {
   if (!q_idx || !w || !k_idx_cache || !block_table || !row_req || !row_len || !scores)
     return DSA_ERR_NULL;
   if (rows < 0 || width < 1 || (width & 3) != 0 || max_pages < 1) return DSA_ERR_SHAPE;
   const int ps = pow2_shift(page_size);
   if (ps < 0) return DSA_ERR_SHAPE;
-  if (blocks) {
-    if (num_blocks < 1 || num_blocks > rows) return DSA_ERR_SHAPE;
-  } else {
-    num_blocks = rows;
-  }
+  if (blocks && (num_blocks < 1 || num_blocks > rows)) return DSA_ERR_SHAPE;
   if (dtype == DSA_BF16) {
     if (!((head_dim == 128 || head_dim == 64) && (num_heads == 32 || num_heads == 64)) ||
         page_size < 16)
@@ -127,28 +128,168 @@ int dsa_indexer_scores(const void* q_idx, const float* w, const void* k_idx_cach
       !aligned(block_table, 4) || !aligned(row_req, 4) || !aligned(row_len, 4) ||
       (blocks && !aligned(blocks, 4)))
     return DSA_ERR_ALIGN;
-  if (rows == 0) return DSA_OK;
-  const int chunk =
-      dtype == DSA_BF16 ? dsa::indexer_chunk_keys(num_blocks, width, num_heads, head_dim) : 256;
-  if ((long long)num_blocks * ((width + chunk - 1) / chunk) > INT32_MAX) return DSA_ERR_SHAPE;
-  hipStream_t st = static_cast<hipStream_t>(stream);
+  const int nb = blocks ? num_blocks : rows;
+  if (rows > 0 && dtype == DSA_BF16) {
+    const int chunk = dsa::indexer_chunk_keys(nb, width, num_heads, head_dim);
+    if ((long long)nb * ((width + chunk - 1) / chunk) > INT32_MAX) return DSA_ERR_SHAPE;
+  } else if (rows > 0 && (long long)nb * ((width + 255) / 256) > INT32_MAX) {
+    return DSA_ERR_SHAPE;
+  }
+  *page_shift = ps;
+  return DSA_OK;
+}
+
+hipError_t indexer_launch(const void* q_idx, const float* w, const void* k_idx_cache,
+                          const int32_t* block_table, const int32_t* row_req,
+                          const int32_t* row_len, const int32_t* blocks, int num_blocks,
+                          float* scores, int rows, int width, int num_heads, int head_dim,
+                          int page_shift, int max_pages, dsa_dtype dtype, hipStream_t st) {
+  const int nb = blocks ? num_blocks : rows;
   if (dtype == DSA_BF16)
-    return launch_status(dsa::launch_indexer_bf16(q_idx, w, k_idx_cache, block_table, row_req,
-                                                  row_len, blocks, num_blocks, scores, width,
-                                                  num_heads, head_dim, ps, max_pages, st));
-  return launch_status(dsa::launch_indexer_f32(
-      static_cast<const float*>(q_idx), w, static_cast<const float*>(k_idx_cache), block_table,
-      row_req, row_len, blocks, num_blocks, scores, width, num_heads, head_dim, ps, max_pages, st));
+    return dsa::launch_indexer_bf16(q_idx, w, k_idx_cache, block_table, row_req, row_len, blocks,
+                                    nb, scores, width, num_heads, head_dim, page_shift, max_pages,
+                                    st);
+  return dsa::launch_indexer_f32(static_cast<const float*>(q_idx), w,
+                                 static_cast<const float*>(k_idx_cache), block_table, row_req,
+                                 row_len, blocks, nb, scores, width, num_heads, head_dim,
+                                 page_shift, max_pages, st);
+}
+
+int topk_check(const float* scores, const int32_t* row_len, int rows, int width, int k,
+               const int32_t* idx) {
+  if (!scores || !row_len || !idx) return DSA_ERR_NULL;
+  if (rows < 0 || width < 1 || (width & 3) != 0 || k < 1 || k > width) return DSA_ERR_SHAPE;
+  if (!aligned(scores, 16) || !aligned(row_len, 4) || !aligned(idx, 4)) return DSA_ERR_ALIGN;
+  return DSA_OK;
+}
+
+// Chunked top-k: chunk >= k, a multiple of 4 (segments start on 16-byte
+// boundaries of the score row); *slots gets the candidate slots needed.
+int topk_chunked_check(int rows, int width, int k, int chunk, long long* slots) {
+  if (rows < 0 || width < 1 || k < 1 || k > width) return DSA_ERR_SHAPE;
+  if (chunk < k || (chunk & 3) != 0 || chunk > (1 << 20)) return DSA_ERR_SHAPE;
+  const long long nseg = dsa::topk_segments(width, chunk);
+  const long long s = (long long)rows * nseg * k;
+  if ((long long)rows * nseg > INT32_MAX || s > (1LL << 40)) return DSA_ERR_SHAPE;
+  *slots = s;
+  return DSA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int dsa_indexer_scores(const void* q_idx, const float* w, const void* k_idx_cache,
+                       const int32_t* block_table, const int32_t* row_req, const int32_t* row_len,
+                       const int32_t* blocks, int num_blocks, float* scores, int rows, int width,
+                       int num_heads, int head_dim, int page_size, int max_pages, dsa_dtype dtype,
+                       void* stream) {
+  int ps = 0;
+  const int st = indexer_check(q_idx, w, k_idx_cache, block_table, row_req, row_len, blocks,
+                               num_blocks, scores, rows, width, num_heads, head_dim, page_size,
+                               max_pages, dtype, &ps);
+  if (st != DSA_OK) return st;
+  if (rows == 0) return DSA_OK;
+  return launch_status(indexer_launch(q_idx, w, k_idx_cache, block_table, row_req, row_len,
+                                      blocks, num_blocks, scores, rows, width, num_heads,
+                                      head_dim, ps, max_pages, dtype,
+                                      static_cast<hipStream_t>(stream)));
 }
 
 int dsa_topk(const float* scores, const int32_t* row_len, int rows, int width, int k,
              int32_t* idx, void* stream) {
-  if (!scores || !row_len || !idx) return DSA_ERR_NULL;
-  if (rows < 0 || width < 1 || (width & 3) != 0 || k < 1 || k > width) return DSA_ERR_SHAPE;
-  if (!aligned(scores, 16) || !aligned(row_len, 4) || !aligned(idx, 4)) return DSA_ERR_ALIGN;
+  const int st = topk_check(scores, row_len, rows, width, k, idx);
+  if (st != DSA_OK) return st;
   if (rows == 0) return DSA_OK;
   return launch_status(
       dsa::launch_topk(scores, row_len, rows, width, k, idx, static_cast<hipStream_t>(stream)));
+}
+
+int dsa_topk_chunked_slots(int rows, int width, int k, int chunk, long long* slots) {
+  if (!slots) return DSA_ERR_NULL;
+  return topk_chunked_check(rows, width, k, chunk, slots);
+}
+
+int dsa_topk_chunked(const float* scores, const int32_t* row_len, int rows, int width, int k,
+                     int chunk, int32_t* cand, long long cand_slots, int32_t* idx, void* stream) {
+  int st = topk_check(scores, row_len, rows, width, k, idx);
+  if (st != DSA_OK) return st;
+  if (!cand) return DSA_ERR_NULL;
+  long long need = 0;
+  st = topk_chunked_check(rows, width, k, chunk, &need);
+  if (st != DSA_OK) return st;
+  if (cand_slots < need) return DSA_ERR_WORKSPACE;
+  if (!aligned(cand, 4)) return DSA_ERR_ALIGN;
+  if (rows == 0) return DSA_OK;
+  return launch_status(dsa::launch_topk_chunked(scores, row_len, rows, width, k, chunk, cand, idx,
+                                                static_cast<hipStream_t>(stream)));
+}
+
+int dsa_topk_chunk_suggest(int rows, int width, int k, int* chunk) {
+  if (!chunk) return DSA_ERR_NULL;
+  if (rows < 0 || width < 1 || k < 1 || k > width) return DSA_ERR_SHAPE;
+  *chunk = dsa::topk_suggest_chunk(rows, width, k);
+  return DSA_OK;
+}
+
+int dsa_select_window_rows(int width, long long score_buffer_bytes, int* window_rows) {
+  if (!window_rows) return DSA_ERR_NULL;
+  if (width < 1 || score_buffer_bytes < 0) return DSA_ERR_SHAPE;
+  const long long w = score_buffer_bytes / ((long long)width * 4);
+  if (w < 1) return DSA_ERR_WORKSPACE;
+  *window_rows = w > INT32_MAX ? INT32_MAX : (int)w;
+  return DSA_OK;
+}
+
+int dsa_indexer_topk_windowed(const void* q_idx, const float* w, const void* k_idx_cache,
+                              const int32_t* block_table, const int32_t* row_req,
+                              const int32_t* row_len, int rows, int width, int num_heads,
+                              int head_dim, int page_size, int max_pages, dsa_dtype dtype, int k,
+                              float* score_buffer, long long score_buffer_bytes, int topk_chunk,
+                              int32_t* cand, long long cand_slots, int32_t* idx, void* stream) {
+  int window = 0;
+  int st = dsa_select_window_rows(width, score_buffer_bytes, &window);
+  if (st != DSA_OK) return st;
+  if (rows < 0) return DSA_ERR_SHAPE;
+  if (window > rows) window = rows;
+  // Every window passes the checks of its first one: row offsets keep the
+  // alignments (a query row is a multiple of 16 bytes).
+  int ps = 0;
+  st = indexer_check(q_idx, w, k_idx_cache, block_table, row_req, row_len, nullptr, 0,
+                     score_buffer, window, width, num_heads, head_dim, page_size, max_pages,
+                     dtype, &ps);
+  if (st != DSA_OK) return st;
+  st = topk_check(score_buffer, row_len, window, width, k, idx);
+  if (st != DSA_OK) return st;
+  if (topk_chunk > 0) {
+    if (!cand) return DSA_ERR_NULL;
+    long long need = 0;
+    st = topk_chunked_check(window, width, k, topk_chunk, &need);
+    if (st != DSA_OK) return st;
+    if (cand_slots < need) return DSA_ERR_WORKSPACE;
+    if (!aligned(cand, 4)) return DSA_ERR_ALIGN;
+  } else if (topk_chunk < 0) {
+    return DSA_ERR_SHAPE;
+  }
+  if (rows == 0) return DSA_OK;
+  const size_t qrow = (size_t)num_heads * head_dim * (dtype == DSA_BF16 ? 2 : 4);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  // Both launches of a window go to one stream, so the next window's scores
+  // overwrite the buffer only after this window's selection has read it.
+  for (int r0 = 0; r0 < rows; r0 += window) {
+    const int n = rows - r0 < window ? rows - r0 : window;
+    hipError_t e = indexer_launch(static_cast<const char*>(q_idx) + (size_t)r0 * qrow,
+                                  w + (size_t)r0 * num_heads, k_idx_cache, block_table,
+                                  row_req + r0, row_len + r0, nullptr, 0, score_buffer, n, width,
+                                  num_heads, head_dim, ps, max_pages, dtype, s);
+    if (e != hipSuccess) return DSA_ERR_LAUNCH;
+    e = topk_chunk > 0 ? dsa::launch_topk_chunked(score_buffer, row_len + r0, n, width, k,
+                                                   topk_chunk, cand, idx + (size_t)r0 * k, s)
+                       : dsa::launch_topk(score_buffer, row_len + r0, n, width, k,
+                                          idx + (size_t)r0 * k, s);
+    if (e != hipSuccess) return DSA_ERR_LAUNCH;
+  }
+  return DSA_OK;
 }
 
 int dsa_sparse_attn(const void* q, const void* k_cache, const void* v_cache,

@@ -113,11 +113,24 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   return base + incl - v;
 }
 
-template <int kThreads, int kVPT>
+// What one workgroup selects from.
+enum TopkMode {
+  kWholeRow = 0,  // row blockIdx.x, positions [0, row_len)
+  kSegment = 1,   // segment c of row r (blockIdx.x = r * nseg + c): positions
+                  // [c * seg, min(row_len, (c + 1) * seg)), output to
+                  // idx + blockIdx.x * k
+  kGather = 2,    // row blockIdx.x over its segments' winners: keys
+                  // scores[row][cand[i]] for the valid prefix of
+                  // cand[row][nseg * k], output the chosen cand entries
+};
+
+template <int kThreads, int kVPT, int kMode = kWholeRow>
 __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores,
                                                        const int32_t* __restrict__ row_len,
                                                        int width, int k,
-                                                       int32_t* __restrict__ idx) {
+                                                       int32_t* __restrict__ idx, int seg,
+                                                       int nseg,
+                                                       const int32_t* __restrict__ cand) {
   constexpr int kTopkThreads = kThreads;
   constexpr int kTopkWaves = kThreads / 64;
   constexpr int kChunk = kThreads * kVPT;
@@ -129,16 +142,43 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   __shared__ uint32_t red[2 * kTopkWaves];
   __shared__ uint32_t pick[3];
 
-  const int r = blockIdx.x;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int L = row_len[r];
-  int32_t* out = idx + (size_t)r * k;
+  // L: keys this workgroup selects from; pos0: position of its first key
+  // (segment mode); gat: the candidate positions (gather mode).
+  int r, L, pos0 = 0;
+  const int32_t* gat = nullptr;
+  int32_t* out;
+  if constexpr (kMode == kSegment) {
+    r = (int)blockIdx.x / nseg;
+    pos0 = ((int)blockIdx.x - r * nseg) * seg;
+    L = min(seg, max(0, row_len[r] - pos0));
+    out = idx + (size_t)blockIdx.x * k;
+  } else {
+    r = blockIdx.x;
+    L = row_len[r];
+    out = idx + (size_t)r * k;
+    if constexpr (kMode == kGather) {
+      // Every segment but a row's last gave k winners (seg >= k), so the
+      // valid candidates are a prefix, in ascending position order.
+      const int n = (L + seg - 1) / seg;
+      L = n == 0 ? 0 : k * (n - 1) + min(k, L - (n - 1) * seg);
+      gat = cand + (size_t)r * nseg * k;
+    }
+  }
+  // Position of key i of this workgroup.
+  auto pos_of = [&](int i) -> int32_t {
+    if constexpr (kMode == kGather) return gat[i];
+    else return pos0 + i;
+  };
   if (L <= k) {
-    for (int i = tid; i < k; i += kTopkThreads) out[i] = i < L ? i : -1;
+    // A segment's padding is never read (stage 2 takes the valid prefix), so
+    // a short or empty segment writes only its positions.
+    const int n = kMode == kSegment ? L : k;
+    for (int i = tid; i < n; i += kTopkThreads) out[i] = i < L ? pos_of(i) : -1;
     return;
   }
-  const float* row = scores + (size_t)r * width;
+  const float* row = scores + (size_t)r * width + pos0;
   const int nchunks = (L + kChunk - 1) / kChunk;
   uint32_t key[kVPT];
   int nv = 0;  // valid positions among this thread's kVPT in the current chunk
@@ -148,7 +188,18 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   auto load_chunk = [&](int c) {
     const int base = c * kChunk + tid * kVPT;
     nv = min(kVPT, max(0, L - base));
-    if (nv == kVPT) {
+    if constexpr (kMode == kGather) {
+      // Candidate positions first (all in flight), then their scores.
+      int32_t at[kVPT];
+#pragma unroll
+      for (int j = 0; j < kVPT; ++j) at[j] = j < nv ? gat[base + j] : 0;
+      // Stage 1 wrote only positions of the row here; the clamp keeps a
+      // broken invariant from ever reading outside it.
+#pragma unroll
+      for (int j = 0; j < kVPT; ++j) at[j] = min(max(at[j], 0), width - 1);
+#pragma unroll
+      for (int j = 0; j < kVPT; ++j) key[j] = j < nv ? order_key(row[at[j]]) : 0u;
+    } else if (nv == kVPT) {
 #pragma unroll
       for (int j = 0; j < kVPT; j += 4) {
         const float4 v = *reinterpret_cast<const float4*>(row + base + j);
@@ -319,10 +370,10 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
       // invariant from ever turning into an out-of-row store.
       if ((gtm >> j) & 1) {
         const uint32_t slot = g + min(e, need);
-        if (slot < (uint32_t)k) out[slot] = base + j;
+        if (slot < (uint32_t)k) out[slot] = pos_of(base + j);
         ++g;
       } else {
-        if (e < need && g + e < (uint32_t)k) out[g + e] = base + j;
+        if (e < need && g + e < (uint32_t)k) out[g + e] = pos_of(base + j);
         ++e;
       }
     }
@@ -344,10 +395,53 @@ hipError_t launch_topk(const float* scores, const int32_t* row_len, int rows, in
     cus = 256;
   if (width > kTopkThreads * 32 && rows <= cus)
     hipLaunchKernelGGL((topk_kernel<kTopkThreads, 64>), dim3(rows), dim3(kTopkThreads), 0, stream,
-                       scores, row_len, width, k, idx);
+                       scores, row_len, width, k, idx, 0, 1, nullptr);
   else
     hipLaunchKernelGGL((topk_kernel<kTopkThreads, 32>), dim3(rows), dim3(kTopkThreads), 0, stream,
-                       scores, row_len, width, k, idx);
+                       scores, row_len, width, k, idx, 0, 1, nullptr);
+  return hipGetLastError();
+}
+
+int topk_segments(int width, int seg) { return (width + seg - 1) / seg; }
+
+int topk_suggest_chunk(int rows, int width, int k) {
+  // One workgroup holds up to 64K keys of a row in registers; longer rows
+  // re-read their chunks on every radix pass, so from there the two-stage
+  // selection over 32768-position segments is faster as long as its first
+  // stage stays within a few workgroups per compute unit.
+  constexpr int kSeg = kTopkThreads * 32;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    cus = 256;
+  if (width <= kTopkThreads * 64 || k > kSeg) return 0;
+  const long long wgs = (long long)rows * topk_segments(width, kSeg);
+  return wgs <= 4LL * cus ? kSeg : 0;
+}
+
+hipError_t launch_topk_chunked(const float* scores, const int32_t* row_len, int rows, int width,
+                               int k, int seg, int32_t* cand, int32_t* idx, hipStream_t stream) {
+  // Stage 1: the exact top-k of every segment of every row (a segment's
+  // winners include every global winner that lies in it), into cand.
+  const int nseg = topk_segments(width, seg);
+  const long long wgs = (long long)rows * nseg;
+  if (seg <= kTopkThreads * 32)
+    hipLaunchKernelGGL((topk_kernel<kTopkThreads, 32, kSegment>), dim3((unsigned)wgs),
+                       dim3(kTopkThreads), 0, stream, scores, row_len, width, k, cand, seg, nseg,
+                       nullptr);
+  else
+    hipLaunchKernelGGL((topk_kernel<kTopkThreads, 64, kSegment>), dim3((unsigned)wgs),
+                       dim3(kTopkThreads), 0, stream, scores, row_len, width, k, cand, seg, nseg,
+                       nullptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // Stage 2: the exact top-k of each row over its segments' winners.
+  if ((long long)nseg * k <= kTopkThreads * 32)
+    hipLaunchKernelGGL((topk_kernel<kTopkThreads, 32, kGather>), dim3(rows), dim3(kTopkThreads), 0,
+                       stream, scores, row_len, width, k, idx, seg, nseg, cand);
+  else
+    hipLaunchKernelGGL((topk_kernel<kTopkThreads, 64, kGather>), dim3(rows), dim3(kTopkThreads), 0,
+                       stream, scores, row_len, width, k, idx, seg, nseg, cand);
   return hipGetLastError();
 }
 

@@ -115,6 +115,14 @@ def headline(seed: int = 20260003) -> Workload:
     return Workload("decode_b64_ctx32k_bf16", "bf16", 64, 64, 8, 128, 64, 128, 2048, prior, new, seed)
 
 
+def long_context(seed: int = 20260006) -> Workload:
+    """Long-context decode: batch 64, every context 204800 (the 200K decode
+    point at which the pages quote their top-k stage), otherwise as the
+    headline workload."""
+    prior, new = _decode([204800] * 64)
+    return Workload("decode_b64_ctx200k_bf16", "bf16", 64, 64, 8, 128, 64, 128, 2048, prior, new, seed)
+
+
 def ragged_lengths(seed: int, batch: int = 64, lo_frac_rows: int = 6) -> list:
     """Context lengths for the ragged batch.
 
@@ -164,6 +172,7 @@ WORKLOADS = {
     "tiny": tiny,
     "decode": decode,
     "headline": headline,
+    "long": long_context,
     "ragged": ragged,
     "mixed": mixed,
 }

@@ -27,6 +27,7 @@ _lib = ctypes.CDLL(LIB_PATH)
 _P = ctypes.c_void_p
 _I = ctypes.c_int
 _F = ctypes.c_float
+_LL = ctypes.c_longlong
 _IP = ctypes.POINTER(ctypes.c_int32)
 
 F32, BF16 = 0, 1
@@ -39,6 +40,12 @@ _SIGS = {
     "dsa_score_width": (_I, [_I, _P, ctypes.POINTER(_I)]),
     "dsa_indexer_scores": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "dsa_topk": (_I, [_P, _P, _I, _I, _I, _P, _P]),
+    "dsa_topk_chunked": (_I, [_P, _P, _I, _I, _I, _I, _P, _LL, _P, _P]),
+    "dsa_topk_chunked_slots": (_I, [_I, _I, _I, _I, ctypes.POINTER(_LL)]),
+    "dsa_topk_chunk_suggest": (_I, [_I, _I, _I, ctypes.POINTER(_I)]),
+    "dsa_indexer_topk_windowed": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
+                                       _P, _LL, _I, _P, _LL, _P, _P]),
+    "dsa_select_window_rows": (_I, [_I, _LL, ctypes.POINTER(_I)]),
     "dsa_sparse_attn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I, _P]),
     "dsa_merge": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _P]),
     "dsa_sparse_attn_splits": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_I)]),
@@ -170,6 +177,61 @@ def topk(scores, row_len, k, idx, stream=None):
     _check("dsa_topk", _lib.dsa_topk(
         _dev(scores, "scores", torch.float32), _dev(row_len, "row_len", torch.int32), rows, width,
         int(k), _dev(idx, "idx", torch.int32), _stream(stream)))
+    return idx
+
+
+def topk_chunked_slots(rows, width, k, chunk) -> int:
+    """dsa_topk_chunked_slots: int32 candidate slots dsa_topk_chunked needs."""
+    out = _LL(0)
+    _check("dsa_topk_chunked_slots", _lib.dsa_topk_chunked_slots(
+        int(rows), int(width), int(k), int(chunk), ctypes.byref(out)))
+    return out.value
+
+
+def topk_chunked(scores, row_len, k, chunk, cand, idx, stream=None):
+    """dsa_topk_chunked: the dsa_topk result in two stages (segment winners in
+    cand, then each row's top-k among them); writes idx [rows][k] in place."""
+    rows, width = scores.shape
+    _check("dsa_topk_chunked", _lib.dsa_topk_chunked(
+        _dev(scores, "scores", torch.float32), _dev(row_len, "row_len", torch.int32), rows, width,
+        int(k), int(chunk), _dev(cand, "cand", torch.int32), int(cand.numel()),
+        _dev(idx, "idx", torch.int32), _stream(stream)))
+    return idx
+
+
+def topk_chunk_suggest(rows, width, k) -> int:
+    """dsa_topk_chunk_suggest: segment length for dsa_topk_chunked, or 0 for dsa_topk."""
+    out = _I(0)
+    _check("dsa_topk_chunk_suggest", _lib.dsa_topk_chunk_suggest(
+        int(rows), int(width), int(k), ctypes.byref(out)))
+    return out.value
+
+
+def select_window_rows(width, score_buffer_bytes) -> int:
+    """dsa_select_window_rows: rows per window for a score buffer of this size."""
+    out = _I(0)
+    _check("dsa_select_window_rows", _lib.dsa_select_window_rows(
+        int(width), int(score_buffer_bytes), ctypes.byref(out)))
+    return out.value
+
+
+def indexer_topk_windowed(q_idx, w, k_idx_cache, block_table, row_req, row_len, width, page_size,
+                          k, score_buffer, idx, topk_chunk=0, cand=None, stream=None):
+    """dsa_indexer_topk_windowed: scores and top-k of every row, a window of
+    rows at a time through score_buffer (any float32 device tensor; its byte
+    size sets the window); writes idx [rows][k] in place."""
+    rows, heads, dim = q_idx.shape
+    if k_idx_cache.dtype != q_idx.dtype:
+        raise TypeError("q_idx and k_idx_cache dtypes differ")
+    _check("dsa_indexer_topk_windowed", _lib.dsa_indexer_topk_windowed(
+        _dev(q_idx, "q_idx"), _dev(w, "w", torch.float32), _dev(k_idx_cache, "k_idx_cache"),
+        _dev(block_table, "block_table", torch.int32), _dev(row_req, "row_req", torch.int32),
+        _dev(row_len, "row_len", torch.int32), rows, int(width), heads, dim, int(page_size),
+        int(block_table.shape[1]), _dtype_code(q_idx), int(k),
+        _dev(score_buffer, "score_buffer", torch.float32), int(score_buffer.numel()) * 4,
+        int(topk_chunk), None if cand is None else _dev(cand, "cand", torch.int32),
+        0 if cand is None else int(cand.numel()), _dev(idx, "idx", torch.int32),
+        _stream(stream)))
     return idx
 
 

@@ -23,10 +23,16 @@ class DsaStep:
     one launch (dsa_sparse_attn_merged) instead of two; None picks the fused
     launch whenever its workgroup of splits can hold the split count the
     library suggests (<= 8 splits, a power of two), and the two launches for
-    small batches that want many splits."""
+    small batches that want many splits. ``topk_chunk`` > 0 selects in two
+    stages over segments of that many positions (dsa_topk_chunked), None
+    takes the library's suggestion for the sizes, 0 the one-pass kernel.
+    ``score_buffer_bytes`` bounds the score memory: rows are scored and
+    selected in windows that fit it (dsa_indexer_topk_windowed), and
+    ``scores`` then holds only the last window's rows."""
 
     def __init__(self, inp, num_splits: int | None = None, block_rows: int = 1,
-                 fused: bool | None = False):
+                 fused: bool | None = False, topk_chunk: int | None = 0,
+                 score_buffer_bytes: int | None = None):
         wl = inp.wl
         dev = inp.q.device
         self.inp = inp
@@ -47,8 +53,22 @@ class DsaStep:
         self.fused = fused
         splits_of = lib.sparse_attn_merged_splits if fused else lib.sparse_attn_splits
         self.num_splits = num_splits or splits_of(*shape)
-        self.scores = torch.empty(self.rows, self.width, dtype=torch.float32, device=dev)
+        # Score rows held at once: all of them, or a window that fits the buffer.
+        self.window_rows = self.rows
+        if score_buffer_bytes is not None:
+            if block_rows > 1:
+                raise ValueError("score windows take no score blocks")
+            self.window_rows = min(self.rows, lib.select_window_rows(self.width, score_buffer_bytes))
+        if topk_chunk is None:
+            topk_chunk = lib.topk_chunk_suggest(self.window_rows, self.width, wl.topk)
+        self.topk_chunk = topk_chunk
+        self.windowed = score_buffer_bytes is not None
+        self.scores = torch.empty(self.window_rows, self.width, dtype=torch.float32, device=dev)
         self.idx = torch.empty(self.rows, wl.topk, dtype=torch.int32, device=dev)
+        self.cand = None
+        if topk_chunk:
+            self.cand = torch.empty(lib.topk_chunked_slots(self.window_rows, self.width, wl.topk,
+                                                           topk_chunk), dtype=torch.int32, device=dev)
         parts = 0 if fused else self.rows
         self.part_o = torch.empty(parts, wl.hq, self.num_splits, wl.d, dtype=torch.float32,
                                   device=dev)
@@ -57,13 +77,26 @@ class DsaStep:
         self.out = torch.empty(self.rows, wl.hq, wl.d, dtype=inp.q.dtype, device=dev)
         self.out_lse = torch.empty(self.rows, wl.hq, dtype=torch.float32, device=dev)
 
-    # The four stages, each one library call.
+    # The four stages, each one library call (with score windows, the first
+    # two are one call that alternates them window by window).
     def indexer(self, stream=None):
         i = self.inp
+        if self.windowed:
+            lib.indexer_topk_windowed(i.qI, i.w, i.kI_cache, i.block_table, self.row_req,
+                                      self.row_len, self.width, self.wl.page, self.wl.topk,
+                                      self.scores, self.idx, topk_chunk=self.topk_chunk,
+                                      cand=self.cand, stream=stream)
+            return
         lib.indexer_scores(i.qI, i.w, i.kI_cache, i.block_table, self.row_req, self.row_len,
                            self.scores, self.wl.page, blocks=self.blocks, stream=stream)
 
     def topk(self, stream=None):
+        if self.windowed:
+            return  # done window by window with the scores
+        if self.topk_chunk:
+            lib.topk_chunked(self.scores, self.row_len, self.wl.topk, self.topk_chunk, self.cand,
+                             self.idx, stream=stream)
+            return
         lib.topk(self.scores, self.row_len, self.wl.topk, self.idx, stream=stream)
 
     def attention(self, stream=None):

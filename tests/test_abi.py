@@ -19,7 +19,7 @@ ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 lib = pytest.importorskip("sparse_attention_decode_02_amd.lib",
                           reason="libdsa.so not built (python -m sparse_attention_decode_02_amd.build)")
 
-OK, NULL, SHAPE, ALIGN, UNSUP = 0, -1, -2, -3, -4
+OK, NULL, SHAPE, ALIGN, UNSUP, WS = 0, -1, -2, -3, -4, -5
 
 
 def test_exports_every_declared_symbol():
@@ -159,6 +159,60 @@ def test_indexer_rejects(kw, code):
 ])
 def test_topk_rejects(kw, code):
     assert lib._lib.dsa_topk(*_topk_args(**kw)) == code
+
+
+def _chunked_args(**kw):
+    a = dict(scores=A, row_len=A, rows=4, width=128, k=16, chunk=32, cand=A, cand_slots=4 * 4 * 16,
+             idx=A, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(scores=None), NULL), (dict(cand=None), NULL), (dict(idx=None), NULL),
+    (dict(chunk=8), SHAPE), (dict(chunk=30), SHAPE), (dict(chunk=(1 << 20) + 4, width=(1 << 20) + 64), SHAPE),
+    (dict(k=0), SHAPE), (dict(width=66), SHAPE), (dict(cand_slots=4 * 4 * 16 - 1), WS),
+    (dict(cand=A + 2), ALIGN), (dict(scores=A + 4), ALIGN), (dict(rows=0), OK),
+])
+def test_topk_chunked_rejects(kw, code):
+    assert lib._lib.dsa_topk_chunked(*_chunked_args(**kw)) == code
+
+
+def test_topk_chunked_slots():
+    assert lib.topk_chunked_slots(4, 128, 16, 32) == 4 * 4 * 16
+    assert lib.topk_chunked_slots(4, 132, 16, 32) == 4 * 5 * 16
+    assert lib.topk_chunked_slots(3, 32768, 2048, 8192) == 3 * 4 * 2048
+    with pytest.raises(lib.DsaError):
+        lib.topk_chunked_slots(4, 128, 16, 8)
+
+
+def test_select_window_rows():
+    assert lib.select_window_rows(128, 128 * 4 * 3 + 5) == 3
+    assert lib.select_window_rows(32768, 1 << 30) == 8192
+    out = ctypes.c_int(0)
+    assert lib._lib.dsa_select_window_rows(128, 511, ctypes.byref(out)) == WS
+    assert lib._lib.dsa_select_window_rows(0, 100, ctypes.byref(out)) == SHAPE
+    assert lib._lib.dsa_select_window_rows(128, 4096, None) == NULL
+
+
+def _windowed_args(**kw):
+    a = dict(q_idx=A, w=A, k_idx_cache=A, block_table=A, row_req=A, row_len=A, rows=4, width=128,
+             num_heads=64, head_dim=128, page_size=64, max_pages=8, dtype=1, k=16, score_buffer=A,
+             score_buffer_bytes=128 * 4 * 2, topk_chunk=0, cand=None, cand_slots=0, idx=A,
+             stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(score_buffer_bytes=511), WS), (dict(score_buffer=None), NULL), (dict(q_idx=None), NULL),
+    (dict(idx=None), NULL), (dict(topk_chunk=-1), SHAPE), (dict(topk_chunk=32), NULL),
+    (dict(topk_chunk=32, cand=A, cand_slots=2 * 4 * 16 - 1), WS), (dict(topk_chunk=8, cand=A, cand_slots=999), SHAPE),
+    (dict(k=0), SHAPE), (dict(head_dim=96), UNSUP), (dict(score_buffer=A + 4), ALIGN),
+    (dict(page_size=48), SHAPE), (dict(rows=-1), SHAPE), (dict(rows=0), OK),
+])
+def test_windowed_rejects(kw, code):
+    assert lib._lib.dsa_indexer_topk_windowed(*_windowed_args(**kw)) == code
 
 
 @pytest.mark.parametrize("kw,code", [

@@ -211,6 +211,97 @@ def test_topk_edges(k, copies):
         assert np.array_equal(got[i], want), f"{name}: first diff at {np.flatnonzero(got[i] != want)[:5]}"
 
 
+def _edge_batch(k):
+    width = 70016
+    cases = _topk_case_rows(width, k)
+    scores = np.full((len(cases), width), np.nan, np.float32)
+    lens = np.zeros(len(cases), np.int32)
+    for i, (_, sc) in enumerate(cases):
+        scores[i, : len(sc)] = sc
+        lens[i] = len(sc)
+    return cases, torch.from_numpy(scores).cuda(), torch.from_numpy(lens).cuda()
+
+
+@pytest.mark.parametrize("k,chunk", [(1, 4), (16, 16), (16, 100), (16, 4096), (2048, 2048),
+                                     (2048, 8192), (2048, 40000)])
+def test_topk_chunked_edges(k, chunk):
+    """The two-stage selection (segment winners, then the row's top-k among
+    them) against the oracle, and bit for bit against the one-pass kernel."""
+    from sparse_attention_decode_02_amd import lib
+    cases, s_d, l_d = _edge_batch(k)
+    _say(f"chunked top-k edges, k {k}, chunk {chunk}, {len(cases)} rows")
+    rows, width = s_d.shape
+    one = torch.full((rows, k), -7, dtype=torch.int32, device="cuda")
+    lib.topk(s_d, l_d, k, one)
+    cand = torch.full((lib.topk_chunked_slots(rows, width, k, chunk),), -9, dtype=torch.int32,
+                      device="cuda")
+    two = torch.full((rows, k), -7, dtype=torch.int32, device="cuda")
+    lib.topk_chunked(s_d, l_d, k, chunk, cand, two)
+    got = two.cpu().numpy()
+    for i, (name, sc) in enumerate(cases):
+        want = O.topk_row(sc, len(sc), k)
+        assert np.array_equal(got[i], want), f"{name}: first diff at {np.flatnonzero(got[i] != want)[:5]}"
+    assert torch.equal(two, one)
+
+
+@pytest.mark.parametrize("window_rows,topk_chunk", [(1, 0), (5, 0), (64, 0), (5, 256), (7, 1024)])
+def test_windowed_matches_full_batch(window_rows, topk_chunk):
+    """Scores and selection in row windows through a bounded buffer give the
+    indices of the whole-batch calls, which the oracle checks row by row."""
+    from sparse_attention_decode_02_amd import lib
+    wl = _small_mixed(seed=21)
+    step = run_step(_host_inputs(wl), num_splits=4)
+    _say(f"windowed indexer + top-k, {window_rows} rows per window, chunk {topk_chunk}")
+    inp = step.inp
+    buf = torch.empty(window_rows * step.width, dtype=torch.float32, device="cuda")
+    assert lib.select_window_rows(step.width, buf.numel() * 4) == window_rows
+    cand = None
+    if topk_chunk:
+        n = lib.topk_chunked_slots(min(window_rows, step.rows), step.width, wl.topk, topk_chunk)
+        cand = torch.empty(n, dtype=torch.int32, device="cuda")
+    idx = torch.full_like(step.idx, -7)
+    lib.indexer_topk_windowed(inp.qI, inp.w, inp.kI_cache, inp.block_table, step.row_req,
+                              step.row_len, step.width, wl.page, wl.topk, buf, idx,
+                              topk_chunk=topk_chunk, cand=cand)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, step.idx)
+    for r in (0, 36, 37, step.rows - 1):
+        check_row(step, r)
+
+
+@pytest.mark.parametrize("kw", [dict(topk_chunk=1024), dict(score_buffer_bytes=6 * 5120 * 4),
+                                dict(score_buffer_bytes=6 * 5120 * 4, topk_chunk=512),
+                                dict(topk_chunk=None)],
+                         ids=["chunked", "windowed", "windowed-chunked", "suggested"])
+def test_step_variants_bit_identical(kw):
+    """The step with the two-stage top-k and/or score windows gives the
+    default step's indices and outputs bit for bit."""
+    inp = _host_inputs(_small_mixed(seed=23, topk=512))
+    ref = run_step(inp, num_splits=4)
+    outs = [t.clone() for t in (ref.idx, ref.out, ref.out_lse)]
+    step = DsaStep(inp, num_splits=4, **kw)
+    _say(f"step variant {kw}: window rows {step.window_rows}, top-k chunk {step.topk_chunk}")
+    step.run()
+    torch.cuda.synchronize()
+    for a, b in zip(outs, (step.idx, step.out, step.out_lse)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+
+
+def test_windowed_fp32_tiny():
+    from sparse_attention_decode_02_amd import lib
+    wl = I.tiny()
+    step = run_step(_host_inputs(wl))
+    inp = step.inp
+    buf = torch.empty(step.width, dtype=torch.float32, device="cuda")  # one row per window
+    idx = torch.full_like(step.idx, -7)
+    lib.indexer_topk_windowed(inp.qI, inp.w, inp.kI_cache, inp.block_table, step.row_req,
+                              step.row_len, step.width, wl.page, wl.topk, buf, idx)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, step.idx)
+    for r in range(step.rows):
+        check_row(step, r)
+
+
 def test_padding_rows_with_zero_length():
     """Rows of length 0 (padding in a fixed-size batch): no score written, all
     slots -1, empty attention (o = 0, lse = -inf), merged output 0."""
@@ -312,12 +403,36 @@ def test_determinism():
 # --------------------------------------------------------------------------
 
 
+def _same_selection_other_ways(step):
+    """At full size, the two-stage top-k and the windowed indexer + top-k
+    reproduce the step's indices bit for bit."""
+    from sparse_attention_decode_02_amd import lib
+    wl, inp = step.wl, step.inp
+    chunk = max(wl.topk, 8192)
+    cand = torch.empty(lib.topk_chunked_slots(step.rows, step.width, wl.topk, chunk),
+                       dtype=torch.int32, device="cuda")
+    idx = torch.full_like(step.idx, -7)
+    lib.topk_chunked(step.scores, step.row_len, wl.topk, chunk, cand, idx)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, step.idx), "two-stage top-k differs"
+    del cand
+    window = 7
+    buf = torch.empty(window * step.width, dtype=torch.float32, device="cuda")
+    idx.fill_(-7)
+    lib.indexer_topk_windowed(inp.qI, inp.w, inp.kI_cache, inp.block_table, step.row_req,
+                              step.row_len, step.width, wl.page, wl.topk, buf, idx)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, step.idx), "windowed indexer + top-k differs"
+    _say(f"  two-stage top-k (chunk {chunk}) and {window}-row windows: identical indices")
+
+
 def _full(wl, rows_fn):
     _say(f"{wl.name}: generating on the device")
     inp = I.generate(wl, "cuda")
     step = run_step(inp, fused=None)  # the launch configuration bench.py times
     _say(f"  rows {step.rows}, width {step.width}, splits {step.num_splits}")
     check_properties(step)
+    _same_selection_other_ways(step)
     rows = rows_fn(step)
     errs = {}
     for r in rows:
@@ -331,6 +446,10 @@ def _full(wl, rows_fn):
 
 def test_headline_full_size():
     _full(I.headline(), lambda s: [0, 1, 37, s.rows - 1])
+
+
+def test_long_context_full_size():
+    _full(I.long_context(), lambda s: [0, s.rows - 1])
 
 
 def test_ragged_full_size():
