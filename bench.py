@@ -279,7 +279,7 @@ def main(argv=None):
             "indexer_block_rows": args.block_rows,
             "attention_merge": "fused" if step.fused else "separate",
             "launch": "graph replay" if args.graph else "stream",
-            "topk": (f"two-stage, {step.topk_chunk}-position segments" if step.topk_chunk
+            "topk_mode": (f"two-stage, {step.topk_chunk}-position segments" if step.topk_chunk
                      else "one pass"),
             "score_rows_per_window": step.window_rows,
         },
