@@ -185,7 +185,9 @@ def main(argv=None):
     ap.add_argument("--workload", default="headline",
                     help="headline (default), decode, tiny, ragged, mixed or long")
     ap.add_argument("--splits", type=int, default=0, help="attention splits (0 = default)")
-    ap.add_argument("--block-rows", type=int, default=1, help="rows per indexer score block")
+    ap.add_argument("--block-rows", type=int, default=8,
+                    help="most rows of one request per indexer score block (1 = none; score "
+                         "windows take none)")
     ap.add_argument("--unfused", action="store_true",
                     help="always run attention and merge as two launches (dsa_sparse_attn + dsa_merge)")
     ap.add_argument("--topk-chunk", type=int, default=-1,
@@ -230,7 +232,8 @@ def main(argv=None):
     wl = I.WORKLOADS[args.workload]()
     print(f"[bench] generating {wl.name} on the device", file=sys.stderr, flush=True)
     inp = I.generate(wl, "cuda")
-    step = DsaStep(inp, num_splits=args.splits or None, block_rows=args.block_rows,
+    block_rows = 1 if args.score_buffer_mib else args.block_rows
+    step = DsaStep(inp, num_splits=args.splits or None, block_rows=block_rows,
                    fused=False if args.unfused else None,
                    topk_chunk=None if args.topk_chunk < 0 else args.topk_chunk,
                    score_buffer_bytes=(args.score_buffer_mib << 20) if args.score_buffer_mib else None)
@@ -276,7 +279,7 @@ def main(argv=None):
             "head_dim": wl.d,
             "indexer": f"{wl.hi}x{wl.di}",
             "attention_splits": step.num_splits,
-            "indexer_block_rows": args.block_rows,
+            "indexer_block_rows": block_rows,
             "attention_merge": "fused" if step.fused else "separate",
             "launch": "graph replay" if args.graph else "stream",
             "topk_mode": (f"two-stage, {step.topk_chunk}-position segments" if step.topk_chunk

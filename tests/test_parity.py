@@ -429,7 +429,7 @@ def _same_selection_other_ways(step):
 def _full(wl, rows_fn):
     _say(f"{wl.name}: generating on the device")
     inp = I.generate(wl, "cuda")
-    step = run_step(inp, fused=None)  # the launch configuration bench.py times
+    step = run_step(inp, fused=None, block_rows=8)  # the launch configuration bench.py times
     _say(f"  rows {step.rows}, width {step.width}, splits {step.num_splits}")
     check_properties(step)
     _same_selection_other_ways(step)
