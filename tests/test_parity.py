@@ -188,13 +188,17 @@ def _topk_case_rows(width, k):
 
 
 @pytest.mark.parametrize("k", [1, 16, 2048])
-@pytest.mark.parametrize("copies", [1, 13], ids=["few-rows", "many-rows"])
-def test_topk_edges(k, copies):
+@pytest.mark.parametrize("copies,width", [(1, 70016), (13, 70016), (1, 4096), (1, 8192), (3, 16384)],
+                         ids=["few-rows", "many-rows", "w4096", "w8192", "w16384"])
+def test_topk_edges(k, copies, width):
     """Edge rows against the oracle. A batch of few wide rows runs the
-    64-keys-per-thread kernel, a batch of more rows than CUs the 32-keys one."""
+    64-keys-per-thread kernel, a batch of more rows than CUs the 32-keys one;
+    score widths up to 16384 run the 512-thread kernels (rows cut to the
+    width)."""
     from sparse_attention_decode_02_amd import lib
-    width = 70016
-    cases = _topk_case_rows(width, k) * copies
+    if k > width:
+        pytest.skip("k > width")
+    cases = [(n, sc[:width]) for n, sc in _topk_case_rows(width, k)] * copies
     _say(f"top-k edges, k {k}, {len(cases)} rows")
     scores = np.full((len(cases), width), np.nan, np.float32)
     lens = np.zeros(len(cases), np.int32)
