@@ -177,7 +177,8 @@ int dsa_topk(const float* scores, const int32_t* row_len, int rows, int width, i
  *   scores   device [rows][width] float32, 16-byte aligned
  *   row_len  device [rows] int32
  *   cand     device int32 workspace of cand_slots entries, at least
- *            rows * ceil(width / chunk) * k (dsa_topk_chunked_slots);
+ *            2 * rows * ceil(width / chunk) * k (dsa_topk_chunked_slots):
+ *            the segment winners' positions, then their sort keys;
  *            overwritten, holds no result
  *   idx      device [rows][k] int32 (output)
  *

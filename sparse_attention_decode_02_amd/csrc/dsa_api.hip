@@ -164,12 +164,13 @@ int topk_check(const float* scores, const int32_t* row_len, int rows, int width,
 }
 
 // Chunked top-k: chunk >= k, a multiple of 4 (segments start on 16-byte
-// boundaries of the score row); *slots gets the candidate slots needed.
+// boundaries of the score row); *slots gets the int32 workspace slots
+// needed (each segment winner's position and key).
 int topk_chunked_check(int rows, int width, int k, int chunk, long long* slots) {
   if (rows < 0 || width < 1 || k < 1 || k > width) return DSA_ERR_SHAPE;
   if (chunk < k || (chunk & 3) != 0 || chunk > (1 << 20)) return DSA_ERR_SHAPE;
   const long long nseg = dsa::topk_segments(width, chunk);
-  const long long s = (long long)rows * nseg * k;
+  const long long s = 2LL * rows * nseg * k;  // positions, then their keys
   if ((long long)rows * nseg > INT32_MAX || s > (1LL << 40)) return DSA_ERR_SHAPE;
   *slots = s;
   return DSA_OK;

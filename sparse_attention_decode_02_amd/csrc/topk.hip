@@ -118,11 +118,12 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
 enum TopkMode {
   kWholeRow = 0,  // row blockIdx.x, positions [0, row_len)
   kSegment = 1,   // segment c of row r (blockIdx.x = r * nseg + c): positions
-                  // [c * seg, min(row_len, (c + 1) * seg)), output to
-                  // idx + blockIdx.x * k
-  kGather = 2,    // row blockIdx.x over its segments' winners: keys
-                  // scores[row][cand[i]] for the valid prefix of
-                  // cand[row][nseg * k], output the chosen cand entries
+                  // [c * seg, min(row_len, (c + 1) * seg)); winners' positions
+                  // to idx + blockIdx.x * k, their keys to aux + blockIdx.x * k
+  kGather = 2,    // row blockIdx.x over its segments' winners: positions at
+                  // aux[row][nseg * k], their keys nseg * k * gridDim.x words
+                  // further, the valid prefix of each; output the chosen
+                  // positions
 };
 
 template <int kThreads, int kVPT, int kMode = kWholeRow>
@@ -130,8 +131,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
                                                        const int32_t* __restrict__ row_len,
                                                        int width, int k,
                                                        int32_t* __restrict__ idx, int seg,
-                                                       int nseg,
-                                                       const int32_t* __restrict__ cand) {
+                                                       int nseg, int32_t* __restrict__ aux) {
   constexpr int kTopkThreads = kThreads;
   constexpr int kTopkWaves = kThreads / 64;
   constexpr int kChunk = kThreads * kVPT;
@@ -148,13 +148,16 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   // L: keys this workgroup selects from; pos0: position of its first key
   // (segment mode); gat: the candidate positions (gather mode).
   int r, L, pos0 = 0;
-  const int32_t* gat = nullptr;
+  const int32_t* gat = nullptr;     // gather mode: the candidates' positions
+  const uint32_t* gkey = nullptr;   // ... and their keys
+  uint32_t* outk = nullptr;         // segment mode: the winners' keys
   int32_t* out;
   if constexpr (kMode == kSegment) {
     r = (int)blockIdx.x / nseg;
     pos0 = ((int)blockIdx.x - r * nseg) * seg;
     L = min(seg, max(0, row_len[r] - pos0));
     out = idx + (size_t)blockIdx.x * k;
+    outk = reinterpret_cast<uint32_t*>(aux) + (size_t)blockIdx.x * k;
   } else {
     r = blockIdx.x;
     L = row_len[r];
@@ -164,7 +167,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
       // valid candidates are a prefix, in ascending position order.
       const int n = (L + seg - 1) / seg;
       L = n == 0 ? 0 : k * (n - 1) + min(k, L - (n - 1) * seg);
-      gat = cand + (size_t)r * nseg * k;
+      gat = aux + (size_t)r * nseg * k;
+      gkey = reinterpret_cast<const uint32_t*>(aux) + (size_t)gridDim.x * nseg * k +
+             (size_t)r * nseg * k;
     }
   }
   // Position of key i of this workgroup.
@@ -173,10 +178,16 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     else return pos0 + i;
   };
   if (L <= k) {
-    // A segment's padding is never read (stage 2 takes the valid prefix), so
-    // a short or empty segment writes only its positions.
-    const int n = kMode == kSegment ? L : k;
-    for (int i = tid; i < n; i += kTopkThreads) out[i] = i < L ? pos_of(i) : -1;
+    if constexpr (kMode == kSegment) {
+      // Every position is a winner; padding is never read (stage 2 takes the
+      // valid prefix), so a short or empty segment writes only its own.
+      for (int i = tid; i < L; i += kTopkThreads) {
+        out[i] = pos0 + i;
+        outk[i] = order_key(scores[(size_t)r * width + pos0 + i]);
+      }
+    } else {
+      for (int i = tid; i < k; i += kTopkThreads) out[i] = i < L ? pos_of(i) : -1;
+    }
     return;
   }
   const float* row = scores + (size_t)r * width + pos0;
@@ -190,16 +201,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     const int base = c * kChunk + tid * kVPT;
     nv = min(kVPT, max(0, L - base));
     if constexpr (kMode == kGather) {
-      // Candidate positions first (all in flight), then their scores.
-      int32_t at[kVPT];
+      // The candidates' keys, written by stage 1 next to their positions.
 #pragma unroll
-      for (int j = 0; j < kVPT; ++j) at[j] = j < nv ? gat[base + j] : 0;
-      // Stage 1 wrote only positions of the row here; the clamp keeps a
-      // broken invariant from ever reading outside it.
-#pragma unroll
-      for (int j = 0; j < kVPT; ++j) at[j] = min(max(at[j], 0), width - 1);
-#pragma unroll
-      for (int j = 0; j < kVPT; ++j) key[j] = j < nv ? order_key(row[at[j]]) : 0u;
+      for (int j = 0; j < kVPT; ++j) key[j] = j < nv ? gkey[base + j] : 0u;
     } else if (nv == kVPT) {
 #pragma unroll
       for (int j = 0; j < kVPT; j += 4) {
@@ -371,10 +375,16 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
       // invariant from ever turning into an out-of-row store.
       if ((gtm >> j) & 1) {
         const uint32_t slot = g + min(e, need);
-        if (slot < (uint32_t)k) out[slot] = pos_of(base + j);
+        if (slot < (uint32_t)k) {
+          out[slot] = pos_of(base + j);
+          if constexpr (kMode == kSegment) outk[slot] = key[j];
+        }
         ++g;
       } else {
-        if (e < need && g + e < (uint32_t)k) out[g + e] = pos_of(base + j);
+        if (e < need && g + e < (uint32_t)k) {
+          out[g + e] = pos_of(base + j);
+          if constexpr (kMode == kSegment) outk[g + e] = key[j];
+        }
         ++e;
       }
     }
@@ -442,17 +452,19 @@ int topk_suggest_chunk(int rows, int width, int k) {
 hipError_t launch_topk_chunked(const float* scores, const int32_t* row_len, int rows, int width,
                                int k, int seg, int32_t* cand, int32_t* idx, hipStream_t stream) {
   // Stage 1: the exact top-k of every segment of every row (a segment's
-  // winners include every global winner that lies in it), into cand.
+  // winners include every global winner that lies in it): positions into
+  // the first half of cand, their keys into the second.
   const int nseg = topk_segments(width, seg);
   const long long wgs = (long long)rows * nseg;
+  int32_t* keys = cand + (size_t)wgs * k;
   if (seg <= kTopkThreads * 32)
     hipLaunchKernelGGL((topk_kernel<kTopkThreads, 32, kSegment>), dim3((unsigned)wgs),
                        dim3(kTopkThreads), 0, stream, scores, row_len, width, k, cand, seg, nseg,
-                       nullptr);
+                       keys);
   else
     hipLaunchKernelGGL((topk_kernel<kTopkThreads, 64, kSegment>), dim3((unsigned)wgs),
                        dim3(kTopkThreads), 0, stream, scores, row_len, width, k, cand, seg, nseg,
-                       nullptr);
+                       keys);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   // Stage 2: the exact top-k of each row over its segments' winners.

@@ -162,7 +162,7 @@ def test_topk_rejects(kw, code):
 
 
 def _chunked_args(**kw):
-    a = dict(scores=A, row_len=A, rows=4, width=128, k=16, chunk=32, cand=A, cand_slots=4 * 4 * 16,
+    a = dict(scores=A, row_len=A, rows=4, width=128, k=16, chunk=32, cand=A, cand_slots=2 * 4 * 4 * 16,
              idx=A, stream=None)
     a.update(kw)
     return list(a.values())
@@ -171,7 +171,7 @@ def _chunked_args(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(scores=None), NULL), (dict(cand=None), NULL), (dict(idx=None), NULL),
     (dict(chunk=8), SHAPE), (dict(chunk=30), SHAPE), (dict(chunk=(1 << 20) + 4, width=(1 << 20) + 64), SHAPE),
-    (dict(k=0), SHAPE), (dict(width=66), SHAPE), (dict(cand_slots=4 * 4 * 16 - 1), WS),
+    (dict(k=0), SHAPE), (dict(width=66), SHAPE), (dict(cand_slots=2 * 4 * 4 * 16 - 1), WS),
     (dict(cand=A + 2), ALIGN), (dict(scores=A + 4), ALIGN), (dict(rows=0), OK),
 ])
 def test_topk_chunked_rejects(kw, code):
@@ -179,9 +179,9 @@ def test_topk_chunked_rejects(kw, code):
 
 
 def test_topk_chunked_slots():
-    assert lib.topk_chunked_slots(4, 128, 16, 32) == 4 * 4 * 16
-    assert lib.topk_chunked_slots(4, 132, 16, 32) == 4 * 5 * 16
-    assert lib.topk_chunked_slots(3, 32768, 2048, 8192) == 3 * 4 * 2048
+    assert lib.topk_chunked_slots(4, 128, 16, 32) == 2 * 4 * 4 * 16
+    assert lib.topk_chunked_slots(4, 132, 16, 32) == 2 * 4 * 5 * 16
+    assert lib.topk_chunked_slots(3, 32768, 2048, 8192) == 2 * 3 * 4 * 2048
     with pytest.raises(lib.DsaError):
         lib.topk_chunked_slots(4, 128, 16, 8)
 
@@ -207,7 +207,7 @@ def _windowed_args(**kw):
 @pytest.mark.parametrize("kw,code", [
     (dict(score_buffer_bytes=511), WS), (dict(score_buffer=None), NULL), (dict(q_idx=None), NULL),
     (dict(idx=None), NULL), (dict(topk_chunk=-1), SHAPE), (dict(topk_chunk=32), NULL),
-    (dict(topk_chunk=32, cand=A, cand_slots=2 * 4 * 16 - 1), WS), (dict(topk_chunk=8, cand=A, cand_slots=999), SHAPE),
+    (dict(topk_chunk=32, cand=A, cand_slots=2 * 2 * 4 * 16 - 1), WS), (dict(topk_chunk=8, cand=A, cand_slots=999), SHAPE),
     (dict(k=0), SHAPE), (dict(head_dim=96), UNSUP), (dict(score_buffer=A + 4), ALIGN),
     (dict(page_size=48), SHAPE), (dict(rows=-1), SHAPE), (dict(rows=0), OK),
 ])
