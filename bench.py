@@ -97,6 +97,48 @@ def time_steps(step, steps, warmup, torch, graph=None):
     return a.elapsed_time(b) / steps  # ms
 
 
+def time_per_step(step, steps, torch, scrub=None):
+    """Each step's time in microseconds (HIP events around it alone); with
+    ``scrub`` (a device tensor larger than L2 and the Infinity Cache) it is
+    read once before every step, outside the events, so the step starts
+    with none of its data cached (and no dirty lines to write back)."""
+    from sparse_attention_decode_02_amd import lib
+    evs = [_events(torch) for _ in range(steps)]
+    sink = torch.empty(4096, dtype=torch.float32, device="cuda")
+    for i in range(steps):
+        if scrub is not None:
+            lib.read_probe(scrub, sink)
+        evs[i][0].record()
+        step.run()
+        evs[i][1].record()
+    torch.cuda.synchronize()
+    return sorted(1000.0 * a.elapsed_time(b) for a, b in evs)
+
+
+def _pct(v, q):
+    return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
+
+
+def read_floor_gbps(torch, mib=1024, reps=10):
+    """A plain streaming read of ``mib`` MiB (dsa_read_probe): the practical
+    read bandwidth the layer's GB/s is compared with."""
+    from sparse_attention_decode_02_amd import lib
+    x = torch.ones(mib << 18, dtype=torch.float32, device="cuda")
+    sink = torch.empty(4096, dtype=torch.float32, device="cuda")
+    for _ in range(3):
+        lib.read_probe(x, sink)
+    torch.cuda.synchronize()
+    a, b = _events(torch)
+    a.record()
+    for _ in range(reps):
+        lib.read_probe(x, sink)
+    b.record()
+    torch.cuda.synchronize()
+    gbps = (mib << 20) * reps / (a.elapsed_time(b) * 1e-3) / 1e9
+    del x
+    return gbps
+
+
 def time_kernels(step, steps, torch):
     """Average duration of each stage's kernel, HIP events on the launch stream."""
     stages = [("indexer", step.indexer), ("topk", step.topk), ("attention", step.attention)]
@@ -180,8 +222,9 @@ def cpu_baseline(step, budget_s, torch):
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=100,
+                    help="untimed steps first (the first ~20 ms of work run at lower clocks)")
     ap.add_argument("--workload", default="headline",
                     help="headline (default), decode, tiny, ragged, mixed or long")
     ap.add_argument("--splits", type=int, default=0, help="attention splits (0 = default)")
@@ -244,6 +287,11 @@ def main(argv=None):
     graph = step.capture() if args.graph else None
     ms = time_steps(step, args.steps, args.warmup, torch, graph)
     kern = time_kernels(step, args.steps, torch)
+    warm = time_per_step(step, args.steps, torch)
+    scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB > L2 + MALL
+    cold = time_per_step(step, args.steps, torch, scrub)
+    del scrub
+    floor = read_floor_gbps(torch)
     layer_us = ms * 1000.0
     ab = algorithmic_bytes(wl, step.row_len_host)
     total_bytes = sum(ab.values())
@@ -253,7 +301,9 @@ def main(argv=None):
     dominant = max(("indexer", "attention"), key=lambda n: kern[n])
     dom_gbps = ab[dominant] / (kern[dominant] * 1e-6) / 1e9
     print(f"[bench] layer {layer_us:.1f} us, {gbps:.0f} GB/s; kernels (us) "
-          + ", ".join(f"{n} {v:.1f}" for n, v in kern.items()), file=sys.stderr, flush=True)
+          + ", ".join(f"{n} {v:.1f}" for n, v in kern.items())
+          + f"; per step warm {_pct(warm, 0.5):.1f} cold {_pct(cold, 0.5):.1f} us; "
+          f"read floor {floor:.0f} GB/s", file=sys.stderr, flush=True)
 
     result = {
         "metric": METRIC,
@@ -288,6 +338,15 @@ def main(argv=None):
         },
         "hbm_gbps": round(gbps, 1),
         "layer_frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+        "per_step_us": {
+            "warm": {"median": round(_pct(warm, 0.5), 2), "p10": round(_pct(warm, 0.1), 2),
+                     "p90": round(_pct(warm, 0.9), 2)},
+            "cold": {"median": round(_pct(cold, 0.5), 2), "p10": round(_pct(cold, 0.1), 2),
+                     "p90": round(_pct(cold, 0.9), 2),
+                     "note": "a 1 GiB buffer is read before each step, outside its events"},
+        },
+        "read_floor_gbps": round(floor, 1),
+        "layer_frac_of_read_floor": round(gbps / floor, 4),
         "algorithmic_bytes": total_bytes,
         "kernels_us": {n: round(v, 2) for n, v in kern.items()},
         "roofline": {

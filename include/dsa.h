@@ -332,6 +332,19 @@ int dsa_sparse_attn_merged_splits(int rows, int num_q_heads, int num_kv_heads, i
 int dsa_merge(const float* part_o, const float* part_lse, int rows, int num_q_heads, int head_dim,
               int num_splits, void* out, float* out_lse, dsa_dtype out_dtype, void* stream);
 
+/* ------------------------------------------------------------------------
+ * dsa_read_probe -- streaming-read probe (not part of the step).
+ *
+ * Reads `bytes` of `src` once with 16-byte loads and writes per-workgroup
+ * fp32 sums to sink[0 .. min(sink_len, 8 * CUs)); its duration gives the
+ * device's practical read bandwidth, the floor the step's bandwidth-bound
+ * kernels are compared with.
+ *
+ *   src   device, 16-byte aligned; bytes a positive multiple of 16
+ *   sink  device float32 [sink_len] (output)
+ * ------------------------------------------------------------------------ */
+int dsa_read_probe(const void* src, long long bytes, float* sink, int sink_len, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -72,4 +72,8 @@ __device__ __forceinline__ int xcd_contiguous(int wg, int n) {
   return (x < r) ? x * (q + 1) + j : r * (q + 1) + (x - r) * q + j;
 }
 
+// Streaming-read probe (benchmark floor): per-workgroup sums into sink[blocks].
+hipError_t launch_read_probe(const void* src, long long bytes, float* sink, int blocks,
+                             hipStream_t stream);
+
 }  // namespace dsa

@@ -46,6 +46,7 @@ _SIGS = {
     "dsa_indexer_topk_windowed": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
                                        _P, _LL, _I, _P, _LL, _P, _P]),
     "dsa_select_window_rows": (_I, [_I, _LL, ctypes.POINTER(_I)]),
+    "dsa_read_probe": (_I, [_P, _LL, _P, _I, _P]),
     "dsa_sparse_attn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I, _P]),
     "dsa_merge": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _P]),
     "dsa_sparse_attn_splits": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_I)]),
@@ -300,3 +301,11 @@ def merge(part_o, part_lse, out, out_lse=None, stream=None):
         d, S, _dev(out, "out"), None if out_lse is None else _dev(out_lse, "out_lse", torch.float32),
         _dtype_code(out), _stream(stream)))
     return out, out_lse
+
+
+def read_probe(src, sink, stream=None):
+    """dsa_read_probe: one streaming read of ``src`` (per-workgroup sums into sink)."""
+    _check("dsa_read_probe", _lib.dsa_read_probe(
+        _dev(src, "src"), int(src.numel() * src.element_size()), _dev(sink, "sink", torch.float32),
+        int(sink.numel()), _stream(stream)))
+    return sink

@@ -195,6 +195,14 @@ def test_select_window_rows():
     assert lib._lib.dsa_select_window_rows(128, 4096, None) == NULL
 
 
+@pytest.mark.parametrize("args,code", [
+    ((None, 64, A, 4), NULL), ((A, 64, None, 4), NULL), ((A, 8, A, 4), SHAPE), ((A, 72, A, 4), SHAPE),
+    ((A, 64, A, 0), SHAPE), ((A + 4, 64, A, 4), ALIGN), ((A, 64, A + 2, 4), ALIGN),
+])
+def test_read_probe_rejects(args, code):
+    assert lib._lib.dsa_read_probe(*args, None) == code
+
+
 def _windowed_args(**kw):
     a = dict(q_idx=A, w=A, k_idx_cache=A, block_table=A, row_req=A, row_len=A, rows=4, width=128,
              num_heads=64, head_dim=128, page_size=64, max_pages=8, dtype=1, k=16, score_buffer=A,

@@ -393,6 +393,17 @@ def test_graph_replay_matches_eager(fused):
         check_row(step, r)
 
 
+def test_read_probe_reads_every_word():
+    """The streaming-read probe of the benchmark sums every 16-byte word once."""
+    from sparse_attention_decode_02_amd import lib
+    x = torch.ones((64 << 20) // 4, dtype=torch.float32, device="cuda")
+    x[-4:] = 3.0  # the tail is read too
+    sink = torch.zeros(4096, dtype=torch.float32, device="cuda")
+    lib.read_probe(x, sink)
+    torch.cuda.synchronize()
+    assert float(sink.double().sum()) == x.numel() + 8
+
+
 def test_determinism():
     inp = _host_inputs(I.decode())
     a = run_step(inp)
