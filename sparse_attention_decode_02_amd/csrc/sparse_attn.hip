@@ -166,11 +166,15 @@ __global__ __launch_bounds__(64 * (FS > 0 ? FS * PP : 1), (sizeof(T) == 2 && D *
   // (row, KV group) pair of this wave; a workgroup's last pairs may not exist
   // (their waves skip the work but still meet the workgroup barriers).
   const int pw = FS > 0 ? wave / FS : 0;  // pair within the workgroup
-  const int pair = FS > 0 ? (int)blockIdx.x * PP + pw : (int)(blockIdx.x / S);
+  // Consecutive work items run on one XCD (workgroup i runs on XCD i % 8), so
+  // the workgroups of a row, which read the same tokens' K/V blocks, share
+  // that XCD's L2 and translation caches.
+  const int wg = xcd_contiguous((int)blockIdx.x, (int)gridDim.x);
+  const int pair = FS > 0 ? wg * PP + pw : wg / S;
   const bool live = FS == 0 || pair < npairs;
   const int g = (live ? pair : 0) % hkv;
   const int r = (live ? pair : 0) / hkv;
-  const int s = FS > 0 ? wave - pw * FS : (int)(blockIdx.x % S);
+  const int s = FS > 0 ? wave - pw * FS : wg % S;
   const uint4* q_lds = q_lds_all[pw];
   float* p_lds = p_lds_all[wave];
   uint32_t* rows_lds = rows_lds_all[wave];
@@ -361,7 +365,7 @@ __global__ __launch_bounds__(64 * (FS > 0 ? FS * PP : 1), (sizeof(T) == 2 && D *
       const int pp = i / (G * D);
       const int hd = i - pp * G * D;
       const int h = hd / D, e = hd - h * D;
-      const int pr = (int)blockIdx.x * PP + pp;
+      const int pr = wg * PP + pp;
       if (pr >= npairs) break;  // the pairs past the end come last
       const int r = pr / hkv, g = pr - r * hkv;
       const int w0 = pp * FS;
