@@ -140,6 +140,19 @@ int dsa_indexer_scores(const void* q_idx, const float* w, const void* k_idx_cach
                        int num_heads, int head_dim, int page_size, int max_pages, dsa_dtype dtype,
                        void* stream);
 
+/* dsa_indexer_scores with a scheduling hint: total_keys = the sum of row_len
+ * over the rows (known on the host from the row plan; 0 = unknown). Rows that
+ * fill at least 90% of rows x width are scored in larger key chunks (no
+ * ragged tail to balance). The scores are identical either way; the launch
+ * shape depends only on the arguments, so a replayed step must pass the same
+ * hint. total_keys outside [0, rows * width]: DSA_ERR_SHAPE. */
+int dsa_indexer_scores_total(const void* q_idx, const float* w, const void* k_idx_cache,
+                             const int32_t* block_table, const int32_t* row_req,
+                             const int32_t* row_len, const int32_t* blocks, int num_blocks,
+                             float* scores, int rows, int width, int num_heads, int head_dim,
+                             int page_size, int max_pages, dsa_dtype dtype, long long total_keys,
+                             void* stream);
+
 /* ------------------------------------------------------------------------
  * dsa_topk -- length-bounded exact top-k.
  *

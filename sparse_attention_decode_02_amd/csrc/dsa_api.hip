@@ -106,7 +106,7 @@ int indexer_check(const void* q_idx, const float* w, const void* k_idx_cache,
                   const int32_t* block_table, const int32_t* row_req, const int32_t* row_len,
                   const int32_t* blocks, int num_blocks, const float* scores, int rows, int width,
                   int num_heads, int head_dim, int page_size, int max_pages, dsa_dtype dtype,
-                  int* page_shift) {
+                  bool full, int* page_shift) {
   if (!q_idx || !w || !k_idx_cache || !block_table || !row_req || !row_len || !scores)
     return DSA_ERR_NULL;
   if (rows < 0 || width < 1 || (width & 3) != 0 || max_pages < 1) return DSA_ERR_SHAPE;
@@ -130,7 +130,7 @@ int indexer_check(const void* q_idx, const float* w, const void* k_idx_cache,
     return DSA_ERR_ALIGN;
   const int nb = blocks ? num_blocks : rows;
   if (rows > 0 && dtype == DSA_BF16) {
-    const int chunk = dsa::indexer_chunk_keys(nb, width, num_heads, head_dim);
+    const int chunk = dsa::indexer_chunk_keys(nb, width, num_heads, head_dim, full);
     if ((long long)nb * ((width + chunk - 1) / chunk) > INT32_MAX) return DSA_ERR_SHAPE;
   } else if (rows > 0 && (long long)nb * ((width + 255) / 256) > INT32_MAX) {
     return DSA_ERR_SHAPE;
@@ -143,12 +143,13 @@ hipError_t indexer_launch(const void* q_idx, const float* w, const void* k_idx_c
                           const int32_t* block_table, const int32_t* row_req,
                           const int32_t* row_len, const int32_t* blocks, int num_blocks,
                           float* scores, int rows, int width, int num_heads, int head_dim,
-                          int page_shift, int max_pages, dsa_dtype dtype, hipStream_t st) {
+                          int page_shift, int max_pages, dsa_dtype dtype, bool full,
+                          hipStream_t st) {
   const int nb = blocks ? num_blocks : rows;
   if (dtype == DSA_BF16)
     return dsa::launch_indexer_bf16(q_idx, w, k_idx_cache, block_table, row_req, row_len, blocks,
                                     nb, scores, width, num_heads, head_dim, page_shift, max_pages,
-                                    st);
+                                    full, st);
   return dsa::launch_indexer_f32(static_cast<const float*>(q_idx), w,
                                  static_cast<const float*>(k_idx_cache), block_table, row_req,
                                  row_len, blocks, nb, scores, width, num_heads, head_dim,
@@ -180,21 +181,35 @@ int topk_chunked_check(int rows, int width, int k, int chunk, long long* slots) 
 
 extern "C" {
 
+int dsa_indexer_scores_total(const void* q_idx, const float* w, const void* k_idx_cache,
+                             const int32_t* block_table, const int32_t* row_req,
+                             const int32_t* row_len, const int32_t* blocks, int num_blocks,
+                             float* scores, int rows, int width, int num_heads, int head_dim,
+                             int page_size, int max_pages, dsa_dtype dtype, long long total_keys,
+                             void* stream) {
+  if (total_keys < 0 || total_keys > (long long)rows * width) return DSA_ERR_SHAPE;
+  // Rows that fill at least 90% of the score width have no ragged tail.
+  const bool full = rows > 0 && total_keys * 10 >= (long long)rows * width * 9;
+  int ps = 0;
+  const int st = indexer_check(q_idx, w, k_idx_cache, block_table, row_req, row_len, blocks,
+                               num_blocks, scores, rows, width, num_heads, head_dim, page_size,
+                               max_pages, dtype, full, &ps);
+  if (st != DSA_OK) return st;
+  if (rows == 0) return DSA_OK;
+  return launch_status(indexer_launch(q_idx, w, k_idx_cache, block_table, row_req, row_len,
+                                      blocks, num_blocks, scores, rows, width, num_heads,
+                                      head_dim, ps, max_pages, dtype, full,
+                                      static_cast<hipStream_t>(stream)));
+}
+
 int dsa_indexer_scores(const void* q_idx, const float* w, const void* k_idx_cache,
                        const int32_t* block_table, const int32_t* row_req, const int32_t* row_len,
                        const int32_t* blocks, int num_blocks, float* scores, int rows, int width,
                        int num_heads, int head_dim, int page_size, int max_pages, dsa_dtype dtype,
                        void* stream) {
-  int ps = 0;
-  const int st = indexer_check(q_idx, w, k_idx_cache, block_table, row_req, row_len, blocks,
-                               num_blocks, scores, rows, width, num_heads, head_dim, page_size,
-                               max_pages, dtype, &ps);
-  if (st != DSA_OK) return st;
-  if (rows == 0) return DSA_OK;
-  return launch_status(indexer_launch(q_idx, w, k_idx_cache, block_table, row_req, row_len,
-                                      blocks, num_blocks, scores, rows, width, num_heads,
-                                      head_dim, ps, max_pages, dtype,
-                                      static_cast<hipStream_t>(stream)));
+  return dsa_indexer_scores_total(q_idx, w, k_idx_cache, block_table, row_req, row_len, blocks,
+                                  num_blocks, scores, rows, width, num_heads, head_dim, page_size,
+                                  max_pages, dtype, 0, stream);
 }
 
 int dsa_topk(const float* scores, const int32_t* row_len, int rows, int width, int k,
@@ -258,7 +273,7 @@ int dsa_indexer_topk_windowed(const void* q_idx, const float* w, const void* k_i
   int ps = 0;
   st = indexer_check(q_idx, w, k_idx_cache, block_table, row_req, row_len, nullptr, 0,
                      score_buffer, window, width, num_heads, head_dim, page_size, max_pages,
-                     dtype, &ps);
+                     dtype, false, &ps);
   if (st != DSA_OK) return st;
   st = topk_check(score_buffer, row_len, window, width, k, idx);
   if (st != DSA_OK) return st;
@@ -282,7 +297,7 @@ int dsa_indexer_topk_windowed(const void* q_idx, const float* w, const void* k_i
     hipError_t e = indexer_launch(static_cast<const char*>(q_idx) + (size_t)r0 * qrow,
                                   w + (size_t)r0 * num_heads, k_idx_cache, block_table,
                                   row_req + r0, row_len + r0, nullptr, 0, score_buffer, n, width,
-                                  num_heads, head_dim, ps, max_pages, dtype, s);
+                                  num_heads, head_dim, ps, max_pages, dtype, false, s);
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
     e = topk_chunk > 0 ? dsa::launch_topk_chunked(score_buffer, row_len + r0, n, width, k,
                                                    topk_chunk, cand, idx + (size_t)r0 * k, s)

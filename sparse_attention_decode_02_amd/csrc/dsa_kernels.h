@@ -15,7 +15,7 @@ int device_capacity(const void* kernel, int block);
 
 // Keys a workgroup of the bf16 indexer covers for one row (a multiple of 64):
 // the chunks of all blocks fill the device about once, at most 4096 keys.
-int indexer_chunk_keys(int num_blocks, int width, int num_heads, int head_dim);
+int indexer_chunk_keys(int num_blocks, int width, int num_heads, int head_dim, bool full);
 
 // Splits of the k slots that fill the device with attention waves about once.
 int attn_default_splits(int rows, int hq, int hkv, int d, int k, bool bf16);
@@ -24,7 +24,7 @@ hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kc
                                const int32_t* bt, const int32_t* row_req, const int32_t* row_len,
                                const int32_t* blocks, int num_blocks, float* scores, int width,
                                int num_heads, int head_dim, int page_shift, int max_pages,
-                               hipStream_t stream);
+                               bool full, hipStream_t stream);
 
 hipError_t launch_indexer_f32(const float* q_idx, const float* w, const float* kcache,
                               const int32_t* bt, const int32_t* row_req, const int32_t* row_len,

@@ -264,18 +264,20 @@ static const void* indexer_kernel_ptr(int num_heads, int head_dim) {
   return nullptr;
 }
 
-int indexer_chunk_keys(int num_blocks, int width, int num_heads, int head_dim) {
+int indexer_chunk_keys(int num_blocks, int width, int num_heads, int head_dim, bool full) {
   // About one round of workgroups over the device: a kernel whose grid is a
   // small multiple of what runs at once leaves most of the chip idle in its
   // last round. Chunks are capped so that long rows spread over many
   // workgroups: with fewer blocks than the device holds, ragged lengths leave
-  // a few long rows as the tail, so the cap is 1024 keys; with more, 2048
-  // (the per-workgroup query load is amortized over more keys).
+  // a few long rows as the tail, so the cap is 1024 keys -- unless the caller
+  // knows the rows fill the score width (`full`), where 2048-key chunks have
+  // no tail to balance and load the query block half as often; with more
+  // blocks than the device holds, 2048.
   const void* kern = indexer_kernel_ptr(num_heads, head_dim);
   int cap = kern ? device_capacity(kern, kIdxThreads) : 0;
   if (cap <= 0) cap = 1024;
   const int per_block = max(1, cap / max(1, num_blocks));
-  const int max_chunk = per_block > 1 ? 1024 : kMaxChunkKeys;
+  const int max_chunk = (per_block > 1 && !full) ? 1024 : kMaxChunkKeys;
   int chunk = (width + per_block - 1) / per_block;
   chunk = ((chunk + 63) / 64) * 64;
   // At least 256 keys (four tiles per wave) to amortize the query load.
@@ -286,8 +288,8 @@ hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kc
                                const int32_t* bt, const int32_t* row_req, const int32_t* row_len,
                                const int32_t* blocks, int num_blocks, float* scores, int width,
                                int num_heads, int head_dim, int page_shift, int max_pages,
-                               hipStream_t stream) {
-  const int chunk = indexer_chunk_keys(num_blocks, width, num_heads, head_dim);
+                               bool full, hipStream_t stream) {
+  const int chunk = indexer_chunk_keys(num_blocks, width, num_heads, head_dim, full);
   const int chunks = (width + chunk - 1) / chunk;
   const int total = num_blocks * chunks;
   const auto* q = static_cast<const uint16_t*>(q_idx);

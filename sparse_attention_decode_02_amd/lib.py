@@ -39,6 +39,8 @@ _SIGS = {
     "dsa_plan_blocks": (_I, [_I, _P, _I, _I, _P, ctypes.POINTER(_I)]),
     "dsa_score_width": (_I, [_I, _P, ctypes.POINTER(_I)]),
     "dsa_indexer_scores": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
+    "dsa_indexer_scores_total": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,
+                                      _LL, _P]),
     "dsa_topk": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "dsa_topk_chunked": (_I, [_P, _P, _I, _I, _I, _I, _P, _LL, _P, _P]),
     "dsa_topk_chunked_slots": (_I, [_I, _I, _I, _I, ctypes.POINTER(_LL)]),
@@ -155,20 +157,26 @@ def score_width(row_len) -> int:
 
 
 def indexer_scores(q_idx, w, k_idx_cache, block_table, row_req, row_len, scores, page_size,
-                   blocks=None, stream=None):
-    """dsa_indexer_scores: writes scores[r][:row_len[r]] in place."""
+                   blocks=None, stream=None, total_keys=None):
+    """dsa_indexer_scores (dsa_indexer_scores_total when ``total_keys``, the
+    host-known sum of the row lengths, is given): writes scores[r][:row_len[r]]
+    in place."""
     rows, heads, dim = q_idx.shape
     dt = _dtype_code(q_idx)
     if k_idx_cache.dtype != q_idx.dtype:
         raise TypeError("q_idx and k_idx_cache dtypes differ")
     nb = 0 if blocks is None else int(blocks.shape[0])
-    _check("dsa_indexer_scores", _lib.dsa_indexer_scores(
-        _dev(q_idx, "q_idx"), _dev(w, "w", torch.float32), _dev(k_idx_cache, "k_idx_cache"),
-        _dev(block_table, "block_table", torch.int32), _dev(row_req, "row_req", torch.int32),
-        _dev(row_len, "row_len", torch.int32),
-        None if blocks is None else _dev(blocks, "blocks", torch.int32), nb,
-        _dev(scores, "scores", torch.float32), rows, int(scores.shape[1]), heads, dim,
-        int(page_size), int(block_table.shape[1]), dt, _stream(stream)))
+    args = [_dev(q_idx, "q_idx"), _dev(w, "w", torch.float32), _dev(k_idx_cache, "k_idx_cache"),
+            _dev(block_table, "block_table", torch.int32), _dev(row_req, "row_req", torch.int32),
+            _dev(row_len, "row_len", torch.int32),
+            None if blocks is None else _dev(blocks, "blocks", torch.int32), nb,
+            _dev(scores, "scores", torch.float32), rows, int(scores.shape[1]), heads, dim,
+            int(page_size), int(block_table.shape[1]), dt]
+    if total_keys is None:
+        _check("dsa_indexer_scores", _lib.dsa_indexer_scores(*args, _stream(stream)))
+    else:
+        _check("dsa_indexer_scores_total",
+               _lib.dsa_indexer_scores_total(*args, int(total_keys), _stream(stream)))
     return scores
 
 

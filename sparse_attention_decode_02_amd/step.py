@@ -41,6 +41,7 @@ class DsaStep:
         self.row_req_host, self.row_len_host = req, ln
         self.rows = len(req)
         self.width = lib.score_width(ln)
+        self.total_keys = int(ln.astype("int64").sum())  # the indexer's scheduling hint
         self.row_req = torch.from_numpy(req).to(dev)
         self.row_len = torch.from_numpy(ln).to(dev)
         self.blocks = None
@@ -88,7 +89,8 @@ class DsaStep:
                                       cand=self.cand, stream=stream)
             return
         lib.indexer_scores(i.qI, i.w, i.kI_cache, i.block_table, self.row_req, self.row_len,
-                           self.scores, self.wl.page, blocks=self.blocks, stream=stream)
+                           self.scores, self.wl.page, blocks=self.blocks, stream=stream,
+                           total_keys=self.total_keys)
 
     def topk(self, stream=None):
         if self.windowed:

@@ -151,6 +151,15 @@ def test_indexer_rejects(kw, code):
     assert lib._lib.dsa_indexer_scores(*_indexer_args(**kw)) == code
 
 
+@pytest.mark.parametrize("total,kw,code", [
+    (-1, {}, SHAPE), (4 * 128 + 1, {}, SHAPE), (4 * 128, dict(q_idx=None), NULL),
+    (4 * 128, dict(width=130), SHAPE), (0, dict(rows=0), OK), (4 * 128, dict(rows=0), SHAPE),
+])
+def test_indexer_total_rejects(total, kw, code):
+    args = _indexer_args(**kw)
+    assert lib._lib.dsa_indexer_scores_total(*args[:-1], total, args[-1]) == code
+
+
 @pytest.mark.parametrize("kw,code", [
     (dict(scores=None), NULL), (dict(row_len=None), NULL), (dict(idx=None), NULL),
     (dict(rows=-1), SHAPE), (dict(width=0), SHAPE), (dict(width=66), SHAPE), (dict(k=0), SHAPE),

@@ -393,6 +393,22 @@ def test_graph_replay_matches_eager(fused):
         check_row(step, r)
 
 
+@pytest.mark.parametrize("wl_fn", [I.decode, lambda: _small_mixed(seed=31)], ids=["decode", "small-mixed"])
+def test_indexer_hint_keeps_scores(wl_fn):
+    """The total-keys hint (larger key chunks for rows that fill the width)
+    changes the launch shape, never a score bit."""
+    from sparse_attention_decode_02_amd import lib
+    step = run_step(_host_inputs(wl_fn()))
+    i = step.inp
+    ref = step.scores.clone()
+    for total in (0, step.total_keys, step.rows * step.width):
+        step.scores.view(torch.int32).fill_(CANARY)
+        lib.indexer_scores(i.qI, i.w, i.kI_cache, i.block_table, step.row_req, step.row_len,
+                           step.scores, step.wl.page, total_keys=total)
+        torch.cuda.synchronize()
+        assert torch.equal(step.scores.view(torch.int32), ref.view(torch.int32)), total
+
+
 def test_read_probe_reads_every_word():
     """The streaming-read probe of the benchmark sums every 16-byte word once."""
     from sparse_attention_decode_02_amd import lib
