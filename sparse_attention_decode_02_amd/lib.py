@@ -105,7 +105,34 @@ def _dev(t: torch.Tensor, name: str, dtype=None):
 def _stream(stream):
     if stream is None:
         return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
+
+
+class Prepared:
+    """One library call with its arguments checked and marshalled once
+    (``prepare=True`` on a kernel wrapper); calling it with a stream (a torch
+    stream, a raw hipStream_t as int, or None for torch's current stream)
+    launches it. The tensors it was built from must stay alive and in place."""
+
+    __slots__ = ("name", "fn", "args")
+
+    def __init__(self, name, fn, args):
+        self.name, self.fn, self.args = name, fn, tuple(args)
+
+    def __call__(self, stream=None):
+        status = self.fn(*self.args, _stream(stream))
+        if status != 0:
+            raise DsaError(self.name, status)
+
+
+def _call(name, args, stream, prepare):
+    fn = getattr(_lib, name)
+    if prepare:
+        return Prepared(name, fn, args)
+    _check(name, fn(*args, _stream(stream)))
+    return None
 
 
 # --------------------------------------------------------------------------
@@ -157,7 +184,7 @@ def score_width(row_len) -> int:
 
 
 def indexer_scores(q_idx, w, k_idx_cache, block_table, row_req, row_len, scores, page_size,
-                   blocks=None, stream=None, total_keys=None):
+                   blocks=None, stream=None, total_keys=None, prepare=False):
     """dsa_indexer_scores (dsa_indexer_scores_total when ``total_keys``, the
     host-known sum of the row lengths, is given): writes scores[r][:row_len[r]]
     in place."""
@@ -173,20 +200,19 @@ def indexer_scores(q_idx, w, k_idx_cache, block_table, row_req, row_len, scores,
             _dev(scores, "scores", torch.float32), rows, int(scores.shape[1]), heads, dim,
             int(page_size), int(block_table.shape[1]), dt]
     if total_keys is None:
-        _check("dsa_indexer_scores", _lib.dsa_indexer_scores(*args, _stream(stream)))
+        p = _call("dsa_indexer_scores", args, stream, prepare)
     else:
-        _check("dsa_indexer_scores_total",
-               _lib.dsa_indexer_scores_total(*args, int(total_keys), _stream(stream)))
-    return scores
+        p = _call("dsa_indexer_scores_total", args + [int(total_keys)], stream, prepare)
+    return p if prepare else scores
 
 
-def topk(scores, row_len, k, idx, stream=None):
+def topk(scores, row_len, k, idx, stream=None, prepare=False):
     """dsa_topk: writes idx [rows][k] in place."""
     rows, width = scores.shape
-    _check("dsa_topk", _lib.dsa_topk(
-        _dev(scores, "scores", torch.float32), _dev(row_len, "row_len", torch.int32), rows, width,
-        int(k), _dev(idx, "idx", torch.int32), _stream(stream)))
-    return idx
+    p = _call("dsa_topk", [_dev(scores, "scores", torch.float32),
+                           _dev(row_len, "row_len", torch.int32), rows, width, int(k),
+                           _dev(idx, "idx", torch.int32)], stream, prepare)
+    return p if prepare else idx
 
 
 def topk_chunked_slots(rows, width, k, chunk) -> int:
@@ -197,15 +223,15 @@ def topk_chunked_slots(rows, width, k, chunk) -> int:
     return out.value
 
 
-def topk_chunked(scores, row_len, k, chunk, cand, idx, stream=None):
+def topk_chunked(scores, row_len, k, chunk, cand, idx, stream=None, prepare=False):
     """dsa_topk_chunked: the dsa_topk result in two stages (segment winners in
     cand, then each row's top-k among them); writes idx [rows][k] in place."""
     rows, width = scores.shape
-    _check("dsa_topk_chunked", _lib.dsa_topk_chunked(
+    p = _call("dsa_topk_chunked", [
         _dev(scores, "scores", torch.float32), _dev(row_len, "row_len", torch.int32), rows, width,
         int(k), int(chunk), _dev(cand, "cand", torch.int32), int(cand.numel()),
-        _dev(idx, "idx", torch.int32), _stream(stream)))
-    return idx
+        _dev(idx, "idx", torch.int32)], stream, prepare)
+    return p if prepare else idx
 
 
 def topk_chunk_suggest(rows, width, k) -> int:
@@ -225,41 +251,41 @@ def select_window_rows(width, score_buffer_bytes) -> int:
 
 
 def indexer_topk_windowed(q_idx, w, k_idx_cache, block_table, row_req, row_len, width, page_size,
-                          k, score_buffer, idx, topk_chunk=0, cand=None, stream=None):
+                          k, score_buffer, idx, topk_chunk=0, cand=None, stream=None,
+                          prepare=False):
     """dsa_indexer_topk_windowed: scores and top-k of every row, a window of
     rows at a time through score_buffer (any float32 device tensor; its byte
     size sets the window); writes idx [rows][k] in place."""
     rows, heads, dim = q_idx.shape
     if k_idx_cache.dtype != q_idx.dtype:
         raise TypeError("q_idx and k_idx_cache dtypes differ")
-    _check("dsa_indexer_topk_windowed", _lib.dsa_indexer_topk_windowed(
+    p = _call("dsa_indexer_topk_windowed", [
         _dev(q_idx, "q_idx"), _dev(w, "w", torch.float32), _dev(k_idx_cache, "k_idx_cache"),
         _dev(block_table, "block_table", torch.int32), _dev(row_req, "row_req", torch.int32),
         _dev(row_len, "row_len", torch.int32), rows, int(width), heads, dim, int(page_size),
         int(block_table.shape[1]), _dtype_code(q_idx), int(k),
         _dev(score_buffer, "score_buffer", torch.float32), int(score_buffer.numel()) * 4,
         int(topk_chunk), None if cand is None else _dev(cand, "cand", torch.int32),
-        0 if cand is None else int(cand.numel()), _dev(idx, "idx", torch.int32),
-        _stream(stream)))
-    return idx
+        0 if cand is None else int(cand.numel()), _dev(idx, "idx", torch.int32)], stream, prepare)
+    return p if prepare else idx
 
 
 def sparse_attn(q, k_cache, v_cache, block_table, row_req, idx, page_size, scale, num_splits,
-                part_o, part_lse, stream=None):
+                part_o, part_lse, stream=None, prepare=False):
     """dsa_sparse_attn: writes part_o [rows][Hq][S][d] and part_lse [rows][Hq][S]."""
     rows, hq, d = q.shape
     hkv = k_cache.shape[2]
     dt = _dtype_code(q)
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype:
         raise TypeError("q, k_cache and v_cache dtypes differ")
-    _check("dsa_sparse_attn", _lib.dsa_sparse_attn(
+    p = _call("dsa_sparse_attn", [
         _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(block_table, "block_table", torch.int32), _dev(row_req, "row_req", torch.int32),
         _dev(idx, "idx", torch.int32), rows, hq, hkv, d, int(idx.shape[1]), int(page_size),
         int(block_table.shape[1]), float(scale), int(num_splits),
-        _dev(part_o, "part_o", torch.float32), _dev(part_lse, "part_lse", torch.float32), dt,
-        _stream(stream)))
-    return part_o, part_lse
+        _dev(part_o, "part_o", torch.float32), _dev(part_lse, "part_lse", torch.float32), dt],
+        stream, prepare)
+    return p if prepare else (part_o, part_lse)
 
 
 def sparse_attn_splits(rows, num_q_heads, num_kv_heads, head_dim, k, dtype) -> int:
@@ -273,7 +299,7 @@ def sparse_attn_splits(rows, num_q_heads, num_kv_heads, head_dim, k, dtype) -> i
 
 
 def sparse_attn_merged(q, k_cache, v_cache, block_table, row_req, idx, page_size, scale,
-                       num_splits, out, out_lse=None, stream=None):
+                       num_splits, out, out_lse=None, stream=None, prepare=False):
     """dsa_sparse_attn_merged: attention and merge in one launch; writes out
     [rows][Hq][d] (and out_lse [rows][Hq] if given)."""
     rows, hq, d = q.shape
@@ -281,14 +307,13 @@ def sparse_attn_merged(q, k_cache, v_cache, block_table, row_req, idx, page_size
     dt = _dtype_code(q)
     if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype or out.dtype != q.dtype:
         raise TypeError("q, k_cache, v_cache and out dtypes differ")
-    _check("dsa_sparse_attn_merged", _lib.dsa_sparse_attn_merged(
+    p = _call("dsa_sparse_attn_merged", [
         _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
         _dev(block_table, "block_table", torch.int32), _dev(row_req, "row_req", torch.int32),
         _dev(idx, "idx", torch.int32), rows, hq, hkv, d, int(idx.shape[1]), int(page_size),
         int(block_table.shape[1]), float(scale), int(num_splits), _dev(out, "out"),
-        None if out_lse is None else _dev(out_lse, "out_lse", torch.float32), dt,
-        _stream(stream)))
-    return out, out_lse
+        None if out_lse is None else _dev(out_lse, "out_lse", torch.float32), dt], stream, prepare)
+    return p if prepare else (out, out_lse)
 
 
 def sparse_attn_merged_splits(rows, num_q_heads, num_kv_heads, head_dim, k, dtype) -> int:
@@ -301,14 +326,14 @@ def sparse_attn_merged_splits(rows, num_q_heads, num_kv_heads, head_dim, k, dtyp
     return out.value
 
 
-def merge(part_o, part_lse, out, out_lse=None, stream=None):
+def merge(part_o, part_lse, out, out_lse=None, stream=None, prepare=False):
     """dsa_merge: writes out [rows][Hq][d] (and out_lse [rows][Hq] if given)."""
     rows, hq, S, d = part_o.shape
-    _check("dsa_merge", _lib.dsa_merge(
+    p = _call("dsa_merge", [
         _dev(part_o, "part_o", torch.float32), _dev(part_lse, "part_lse", torch.float32), rows, hq,
         d, S, _dev(out, "out"), None if out_lse is None else _dev(out_lse, "out_lse", torch.float32),
-        _dtype_code(out), _stream(stream)))
-    return out, out_lse
+        _dtype_code(out)], stream, prepare)
+    return p if prepare else (out, out_lse)
 
 
 def read_probe(src, sink, stream=None):

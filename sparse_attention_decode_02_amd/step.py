@@ -78,50 +78,66 @@ class DsaStep:
         self.out = torch.empty(self.rows, wl.hq, wl.d, dtype=inp.q.dtype, device=dev)
         self.out_lse = torch.empty(self.rows, wl.hq, dtype=torch.float32, device=dev)
 
-    # The four stages, each one library call (with score windows, the first
-    # two are one call that alternates them window by window).
-    def indexer(self, stream=None):
-        i = self.inp
+        self._prepare()
+
+    def _prepare(self):
+        """Checks and marshals every library call of the step once; each stage
+        then only launches (the binding's per-call tensor checks would
+        otherwise cost more host time than a small step takes on the GPU)."""
+        i, wl = self.inp, self.wl
+        self._calls = {"indexer": None, "topk": None, "attention": None, "merge": None}
         if self.windowed:
-            lib.indexer_topk_windowed(i.qI, i.w, i.kI_cache, i.block_table, self.row_req,
-                                      self.row_len, self.width, self.wl.page, self.wl.topk,
-                                      self.scores, self.idx, topk_chunk=self.topk_chunk,
-                                      cand=self.cand, stream=stream)
-            return
-        lib.indexer_scores(i.qI, i.w, i.kI_cache, i.block_table, self.row_req, self.row_len,
-                           self.scores, self.wl.page, blocks=self.blocks, stream=stream,
-                           total_keys=self.total_keys)
+            # Indexer and top-k as one call that alternates them window by window.
+            self._calls["indexer"] = lib.indexer_topk_windowed(
+                i.qI, i.w, i.kI_cache, i.block_table, self.row_req, self.row_len, self.width,
+                wl.page, wl.topk, self.scores, self.idx, topk_chunk=self.topk_chunk,
+                cand=self.cand, prepare=True)
+        else:
+            self._calls["indexer"] = lib.indexer_scores(
+                i.qI, i.w, i.kI_cache, i.block_table, self.row_req, self.row_len, self.scores,
+                wl.page, blocks=self.blocks, total_keys=self.total_keys, prepare=True)
+            if self.topk_chunk:
+                self._calls["topk"] = lib.topk_chunked(self.scores, self.row_len, wl.topk,
+                                                       self.topk_chunk, self.cand, self.idx,
+                                                       prepare=True)
+            else:
+                self._calls["topk"] = lib.topk(self.scores, self.row_len, wl.topk, self.idx,
+                                               prepare=True)
+        if self.fused:
+            self._calls["attention"] = lib.sparse_attn_merged(
+                i.q, i.k_cache, i.v_cache, i.block_table, self.row_req, self.idx, wl.page,
+                wl.attn_scale, self.num_splits, self.out, self.out_lse, prepare=True)
+        else:
+            self._calls["attention"] = lib.sparse_attn(
+                i.q, i.k_cache, i.v_cache, i.block_table, self.row_req, self.idx, wl.page,
+                wl.attn_scale, self.num_splits, self.part_o, self.part_lse, prepare=True)
+            self._calls["merge"] = lib.merge(self.part_o, self.part_lse, self.out, self.out_lse,
+                                             prepare=True)
+        self._seq = [c for c in self._calls.values() if c is not None]
+
+    # The four stages, each one library call (with score windows, indexer and
+    # top-k are one call; with the fused attention, attention and merge).
+    def _stage(self, name, stream):
+        c = self._calls[name]
+        if c is not None:
+            c(stream)
+
+    def indexer(self, stream=None):
+        self._stage("indexer", stream)
 
     def topk(self, stream=None):
-        if self.windowed:
-            return  # done window by window with the scores
-        if self.topk_chunk:
-            lib.topk_chunked(self.scores, self.row_len, self.wl.topk, self.topk_chunk, self.cand,
-                             self.idx, stream=stream)
-            return
-        lib.topk(self.scores, self.row_len, self.wl.topk, self.idx, stream=stream)
+        self._stage("topk", stream)
 
     def attention(self, stream=None):
-        i = self.inp
-        if self.fused:
-            lib.sparse_attn_merged(i.q, i.k_cache, i.v_cache, i.block_table, self.row_req,
-                                   self.idx, self.wl.page, self.wl.attn_scale, self.num_splits,
-                                   self.out, self.out_lse, stream=stream)
-            return
-        lib.sparse_attn(i.q, i.k_cache, i.v_cache, i.block_table, self.row_req, self.idx,
-                        self.wl.page, self.wl.attn_scale, self.num_splits, self.part_o,
-                        self.part_lse, stream=stream)
+        self._stage("attention", stream)
 
     def merge(self, stream=None):
-        if self.fused:
-            return  # done by the attention launch
-        lib.merge(self.part_o, self.part_lse, self.out, self.out_lse, stream=stream)
+        self._stage("merge", stream)
 
     def run(self, stream=None):
-        self.indexer(stream)
-        self.topk(stream)
-        self.attention(stream)
-        self.merge(stream)
+        h = lib._stream(stream)  # resolved once for the step's launches
+        for c in self._seq:
+            c(h)
         return self.out
 
     def capture(self):
