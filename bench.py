@@ -226,11 +226,10 @@ def main(argv=None):
     ap.add_argument("--warmup", type=int, default=100,
                     help="untimed steps first (the first ~20 ms of work run at lower clocks)")
     ap.add_argument("--workload", default="headline",
-                    help="headline (default), decode, tiny, ragged, mixed or long")
+                    help="headline (default), decode, tiny, ragged, mixed, long or prefill_1m")
     ap.add_argument("--splits", type=int, default=0, help="attention splits (0 = default)")
     ap.add_argument("--block-rows", type=int, default=8,
-                    help="most rows of one request per indexer score block (1 = none; score "
-                         "windows take none)")
+                    help="most rows of one request per indexer score block (1 = none)")
     ap.add_argument("--unfused", action="store_true",
                     help="always run attention and merge as two launches (dsa_sparse_attn + dsa_merge)")
     ap.add_argument("--topk-chunk", type=int, default=-1,
@@ -275,7 +274,7 @@ def main(argv=None):
     wl = I.WORKLOADS[args.workload]()
     print(f"[bench] generating {wl.name} on the device", file=sys.stderr, flush=True)
     inp = I.generate(wl, "cuda")
-    block_rows = 1 if args.score_buffer_mib else args.block_rows
+    block_rows = args.block_rows
     step = DsaStep(inp, num_splits=args.splits or None, block_rows=block_rows,
                    fused=False if args.unfused else None,
                    topk_chunk=None if args.topk_chunk < 0 else args.topk_chunk,

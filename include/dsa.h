@@ -205,9 +205,12 @@ int dsa_topk_chunked(const float* scores, const int32_t* row_len, int rows, int 
 int dsa_topk_chunked_slots(int rows, int width, int k, int chunk, long long* slots);
 
 /* The segment length at which dsa_topk_chunked is expected to beat dsa_topk
- * on the current device for these sizes (rows longer than one workgroup holds
- * in registers, few enough segments to run at once), or 0 (host). */
-int dsa_topk_chunk_suggest(int rows, int width, int k, int* chunk);
+ * on the current device for these sizes, or 0 (host): rows longer than one
+ * workgroup holds in registers, and either rows that fill the width
+ * (total_keys, the sum of the row lengths, >= 90% of rows * width) or few
+ * enough segments to run at once. total_keys outside [0, rows * width]:
+ * DSA_ERR_SHAPE. */
+int dsa_topk_chunk_suggest(int rows, int width, int k, long long total_keys, int* chunk);
 
 /* ------------------------------------------------------------------------
  * dsa_indexer_topk_windowed -- indexer scores and top-k in row windows.
@@ -215,16 +218,21 @@ int dsa_topk_chunk_suggest(int rows, int width, int k, int* chunk);
  * Commit "Score and select rows in windows whose score buffer fits ...": the
  * rows are scored and selected a window at a time through one caller-given
  * score buffer, so its size bounds the score memory at any context length.
- * A window holds window_rows = score_buffer_bytes / (width * 4) rows
- * (dsa_select_window_rows); the window count depends only on rows and width,
- * so the launch sequence is the same for every step of those sizes. Each
- * window runs dsa_indexer_scores on rows [r0, r0 + n) into the buffer, then
- * dsa_topk (topk_chunk == 0) or dsa_topk_chunked (topk_chunk > 0, with cand
- * sized for one window) into idx rows [r0, r0 + n). Results equal those of
+ * A window holds at most window_rows = score_buffer_bytes / (width * 4) rows
+ * (dsa_select_window_rows); with score blocks it is a run of whole blocks.
+ * The window count depends only on the sizes and the block plan, so the
+ * launch sequence is the same for every step of those sizes. Each window
+ * runs the indexer on its rows into the buffer, then dsa_topk
+ * (topk_chunk == 0) or dsa_topk_chunked (topk_chunk > 0, with cand sized for
+ * one window) into those rows of idx. Results equal those of
  * dsa_indexer_scores over all rows followed by the same selection.
  *
  *   q_idx, w, k_idx_cache, block_table, row_req, row_len: as for
- *            dsa_indexer_scores (all rows; no score blocks)
+ *            dsa_indexer_scores (all rows)
+ *   blocks_host, blocks_dev, num_blocks: optional score blocks (the
+ *            dsa_plan_blocks plan, on the host and a device copy of it), or
+ *            0 and NULL for none; the plan must cover the rows in order, and
+ *            a block longer than a window returns DSA_ERR_WORKSPACE
  *   score_buffer  device float32 workspace of score_buffer_bytes, 16-byte
  *            aligned; overwritten, holds no result
  *   cand, cand_slots  as for dsa_topk_chunked, for window_rows rows (unused,
@@ -235,10 +243,12 @@ int dsa_topk_chunk_suggest(int rows, int width, int k, int* chunk);
  * ------------------------------------------------------------------------ */
 int dsa_indexer_topk_windowed(const void* q_idx, const float* w, const void* k_idx_cache,
                               const int32_t* block_table, const int32_t* row_req,
-                              const int32_t* row_len, int rows, int width, int num_heads,
-                              int head_dim, int page_size, int max_pages, dsa_dtype dtype, int k,
-                              float* score_buffer, long long score_buffer_bytes, int topk_chunk,
-                              int32_t* cand, long long cand_slots, int32_t* idx, void* stream);
+                              const int32_t* row_len, const int32_t* blocks_host,
+                              const int32_t* blocks_dev, int num_blocks, int rows, int width,
+                              int num_heads, int head_dim, int page_size, int max_pages,
+                              dsa_dtype dtype, int k, float* score_buffer,
+                              long long score_buffer_bytes, int topk_chunk, int32_t* cand,
+                              long long cand_slots, int32_t* idx, void* stream);
 
 /* Rows per window for a score buffer of score_buffer_bytes (host). */
 int dsa_select_window_rows(int width, long long score_buffer_bytes, int* window_rows);

@@ -70,16 +70,16 @@ hipError_t indexer_launch(const void* q_idx, const float* w, const void* k_idx_c
                           const int32_t* row_len, const int32_t* blocks, int num_blocks,
                           float* scores, int rows, int width, int num_heads, int head_dim,
                           int page_shift, int max_pages, dsa_dtype dtype, bool full,
-                          hipStream_t st) {
+                          hipStream_t st, int score_row0 = 0) {
   const int nb = blocks ? num_blocks : rows;
   if (dtype == DSA_BF16)
     return dsa::launch_indexer_bf16(q_idx, w, k_idx_cache, block_table, row_req, row_len, blocks,
                                     nb, scores, width, num_heads, head_dim, page_shift, max_pages,
-                                    full, st);
+                                    full, score_row0, st);
   return dsa::launch_indexer_f32(static_cast<const float*>(q_idx), w,
                                  static_cast<const float*>(k_idx_cache), block_table, row_req,
                                  row_len, blocks, nb, scores, width, num_heads, head_dim,
-                                 page_shift, max_pages, st);
+                                 page_shift, max_pages, score_row0, st);
 }
 
 int topk_check(const float* scores, const int32_t* row_len, int rows, int width, int k,
@@ -167,31 +167,59 @@ int dsa_topk_chunked(const float* scores, const int32_t* row_len, int rows, int 
                                                 static_cast<hipStream_t>(stream)));
 }
 
-int dsa_topk_chunk_suggest(int rows, int width, int k, int* chunk) {
+int dsa_topk_chunk_suggest(int rows, int width, int k, long long total_keys, int* chunk) {
   if (!chunk) return DSA_ERR_NULL;
   if (rows < 0 || width < 1 || k < 1 || k > width) return DSA_ERR_SHAPE;
-  *chunk = dsa::topk_suggest_chunk(rows, width, k);
+  if (total_keys < 0 || total_keys > (long long)rows * width) return DSA_ERR_SHAPE;
+  const bool full = rows > 0 && total_keys * 10 >= (long long)rows * width * 9;
+  *chunk = dsa::topk_suggest_chunk(rows, width, k, full);
   return DSA_OK;
 }
 
 
+// Windows over a score-block plan: each window is a run of whole blocks
+// holding at most `window` rows. blocks_host must cover rows 0..rows-1 in
+// order; a block longer than a window cannot be placed.
+static int plan_block_windows(const int32_t* blocks, int num_blocks, int rows, int window) {
+  int next = 0;
+  for (int b = 0; b < num_blocks; ++b) {
+    const int first = blocks[2 * b], n = blocks[2 * b + 1];
+    if (first != next || n < 1 || n > rows - next) return DSA_ERR_SHAPE;
+    if (n > window) return DSA_ERR_WORKSPACE;
+    next += n;
+  }
+  return next == rows ? DSA_OK : DSA_ERR_SHAPE;
+}
+
 int dsa_indexer_topk_windowed(const void* q_idx, const float* w, const void* k_idx_cache,
                               const int32_t* block_table, const int32_t* row_req,
-                              const int32_t* row_len, int rows, int width, int num_heads,
-                              int head_dim, int page_size, int max_pages, dsa_dtype dtype, int k,
-                              float* score_buffer, long long score_buffer_bytes, int topk_chunk,
-                              int32_t* cand, long long cand_slots, int32_t* idx, void* stream) {
+                              const int32_t* row_len, const int32_t* blocks_host,
+                              const int32_t* blocks_dev, int num_blocks, int rows, int width,
+                              int num_heads, int head_dim, int page_size, int max_pages,
+                              dsa_dtype dtype, int k, float* score_buffer,
+                              long long score_buffer_bytes, int topk_chunk, int32_t* cand,
+                              long long cand_slots, int32_t* idx, void* stream) {
   int window = 0;
   int st = dsa_select_window_rows(width, score_buffer_bytes, &window);
   if (st != DSA_OK) return st;
   if (rows < 0) return DSA_ERR_SHAPE;
   if (window > rows) window = rows;
-  // Every window passes the checks of its first one: row offsets keep the
+  const bool with_blocks = num_blocks > 0;
+  if (with_blocks) {
+    if (!blocks_host || !blocks_dev) return DSA_ERR_NULL;
+    if (num_blocks > rows) return DSA_ERR_SHAPE;
+    st = plan_block_windows(blocks_host, num_blocks, rows, window);
+    if (st != DSA_OK) return st;
+  } else if (num_blocks < 0) {
+    return DSA_ERR_SHAPE;
+  }
+  // Every window passes the checks of the whole call: row offsets keep the
   // alignments (a query row is a multiple of 16 bytes).
   int ps = 0;
-  st = indexer_check(q_idx, w, k_idx_cache, block_table, row_req, row_len, nullptr, 0,
-                     score_buffer, window, width, num_heads, head_dim, page_size, max_pages,
-                     dtype, false, &ps);
+  st = indexer_check(q_idx, w, k_idx_cache, block_table, row_req, row_len,
+                     with_blocks ? blocks_dev : nullptr, num_blocks, score_buffer,
+                     with_blocks ? rows : window, width, num_heads, head_dim, page_size,
+                     max_pages, dtype, false, &ps);
   if (st != DSA_OK) return st;
   st = topk_check(score_buffer, row_len, window, width, k, idx);
   if (st != DSA_OK) return st;
@@ -210,6 +238,28 @@ int dsa_indexer_topk_windowed(const void* q_idx, const float* w, const void* k_i
   hipStream_t s = static_cast<hipStream_t>(stream);
   // Both launches of a window go to one stream, so the next window's scores
   // overwrite the buffer only after this window's selection has read it.
+  auto select = [&](int r0, int n) {
+    return topk_chunk > 0 ? dsa::launch_topk_chunked(score_buffer, row_len + r0, n, width, k,
+                                                      topk_chunk, cand, idx + (size_t)r0 * k, s)
+                          : dsa::launch_topk(score_buffer, row_len + r0, n, width, k,
+                                             idx + (size_t)r0 * k, s);
+  };
+  if (with_blocks) {
+    // Whole blocks per window; the kernel reads rows at their own index and
+    // writes scores from the window's first row.
+    for (int b0 = 0; b0 < num_blocks;) {
+      const int r0 = blocks_host[2 * b0];
+      int b1 = b0, n = 0;
+      while (b1 < num_blocks && n + blocks_host[2 * b1 + 1] <= window) n += blocks_host[2 * b1++ + 1];
+      hipError_t e = indexer_launch(q_idx, w, k_idx_cache, block_table, row_req, row_len,
+                                    blocks_dev + 2 * (size_t)b0, b1 - b0, score_buffer, n, width,
+                                    num_heads, head_dim, ps, max_pages, dtype, false, s, r0);
+      if (e != hipSuccess) return DSA_ERR_LAUNCH;
+      if (select(r0, n) != hipSuccess) return DSA_ERR_LAUNCH;
+      b0 = b1;
+    }
+    return DSA_OK;
+  }
   for (int r0 = 0; r0 < rows; r0 += window) {
     const int n = rows - r0 < window ? rows - r0 : window;
     hipError_t e = indexer_launch(static_cast<const char*>(q_idx) + (size_t)r0 * qrow,
@@ -217,11 +267,7 @@ int dsa_indexer_topk_windowed(const void* q_idx, const float* w, const void* k_i
                                   row_req + r0, row_len + r0, nullptr, 0, score_buffer, n, width,
                                   num_heads, head_dim, ps, max_pages, dtype, false, s);
     if (e != hipSuccess) return DSA_ERR_LAUNCH;
-    e = topk_chunk > 0 ? dsa::launch_topk_chunked(score_buffer, row_len + r0, n, width, k,
-                                                   topk_chunk, cand, idx + (size_t)r0 * k, s)
-                       : dsa::launch_topk(score_buffer, row_len + r0, n, width, k,
-                                          idx + (size_t)r0 * k, s);
-    if (e != hipSuccess) return DSA_ERR_LAUNCH;
+    if (select(r0, n) != hipSuccess) return DSA_ERR_LAUNCH;
   }
   return DSA_OK;
 }

@@ -24,20 +24,20 @@ hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kc
                                const int32_t* bt, const int32_t* row_req, const int32_t* row_len,
                                const int32_t* blocks, int num_blocks, float* scores, int width,
                                int num_heads, int head_dim, int page_shift, int max_pages,
-                               bool full, hipStream_t stream);
+                               bool full, int score_row0, hipStream_t stream);
 
 hipError_t launch_indexer_f32(const float* q_idx, const float* w, const float* kcache,
                               const int32_t* bt, const int32_t* row_req, const int32_t* row_len,
                               const int32_t* blocks, int num_blocks, float* scores, int width,
                               int num_heads, int head_dim, int page_shift, int max_pages,
-                              hipStream_t stream);
+                              int score_row0, hipStream_t stream);
 
 hipError_t launch_topk(const float* scores, const int32_t* row_len, int rows, int width, int k,
                        int32_t* idx, hipStream_t stream);
 // Segments of `seg` positions per row of `width` (the stage-1 workgroups per row).
 int topk_segments(int width, int seg);
 // Segment length for dsa_topk_chunked when it beats the one-pass kernel, else 0.
-int topk_suggest_chunk(int rows, int width, int k);
+int topk_suggest_chunk(int rows, int width, int k, bool full);
 // Two-stage exact top-k: per-segment winners into cand [rows][nseg][k], then
 // each row's top-k over them into idx. Requires seg >= k.
 hipError_t launch_topk_chunked(const float* scores, const int32_t* row_len, int rows, int width,

@@ -61,7 +61,7 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_mfma_kernel(
     const uint16_t* __restrict__ kc, const int32_t* __restrict__ bt,
     const int32_t* __restrict__ row_req, const int32_t* __restrict__ row_len,
     const int32_t* __restrict__ blocks, float* __restrict__ scores, int width, int page_shift,
-    int max_pages, int chunk_keys, int chunks, int total) {
+    int max_pages, int chunk_keys, int chunks, int total, int score_row0) {
   constexpr int H = HT * 16;
   constexpr int KS = DI / 32;  // MFMA steps per head tile
   constexpr int QST = DI + 8;  // padded LDS row (elements): the 16 rows read together hit distinct banks
@@ -97,7 +97,7 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_mfma_kernel(
     const int req = row_req[r];
     const int32_t* btr = bt + (size_t)req * max_pages;
     const int end = min(L, chunk0 + chunk_keys);
-    float* out = scores + (size_t)r * width;
+    float* out = scores + (size_t)(r - score_row0) * width;  // rows of a window from its first
 
     // Key fragments of the 16-key tile at `base` (base is wave-uniform). The
     // tile lies inside one page (page size >= 16), whose number is one scalar
@@ -201,7 +201,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_f32_kernel(
     const int32_t* __restrict__ bt, const int32_t* __restrict__ row_req,
     const int32_t* __restrict__ row_len, const int32_t* __restrict__ blocks,
     float* __restrict__ scores, int width, int H, int page_shift, int max_pages, int chunk_keys,
-    int chunks, int total) {
+    int chunks, int total, int score_row0) {
   __shared__ float q_lds[64 * DI];
   __shared__ float w_lds[64];
   const int item = xcd_contiguous(blockIdx.x, total);
@@ -243,7 +243,7 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_f32_kernel(
         for (int j = 0; j < DI; ++j) dot = fmaf(q_lds[h * DI + j], kv[j], dot);
         tot += w_lds[h] * fmaxf(dot, 0.0f);
       }
-      scores[(size_t)r * width + s] = tot + 0.0f;
+      scores[(size_t)(r - score_row0) * width + s] = tot + 0.0f;
     }
   }
 }
@@ -288,7 +288,7 @@ hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kc
                                const int32_t* bt, const int32_t* row_req, const int32_t* row_len,
                                const int32_t* blocks, int num_blocks, float* scores, int width,
                                int num_heads, int head_dim, int page_shift, int max_pages,
-                               bool full, hipStream_t stream) {
+                               bool full, int score_row0, hipStream_t stream) {
   const int chunk = indexer_chunk_keys(num_blocks, width, num_heads, head_dim, full);
   const int chunks = (width + chunk - 1) / chunk;
   const int total = num_blocks * chunks;
@@ -297,7 +297,7 @@ hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kc
 #define DSA_IDX_LAUNCH(HT, DI)                                                                 \
   hipLaunchKernelGGL((indexer_mfma_kernel<HT, DI>), dim3(total), dim3(kIdxThreads), 0, stream, \
                      q, w, k, bt, row_req, row_len, blocks, scores, width, page_shift,         \
-                     max_pages, chunk, chunks, total)
+                     max_pages, chunk, chunks, total, score_row0)
   if (num_heads == 64 && head_dim == 128) DSA_IDX_LAUNCH(4, 128);
   else if (num_heads == 32 && head_dim == 128) DSA_IDX_LAUNCH(2, 128);
   else if (num_heads == 64 && head_dim == 64) DSA_IDX_LAUNCH(4, 64);
@@ -311,14 +311,14 @@ hipError_t launch_indexer_f32(const float* q_idx, const float* w, const float* k
                               const int32_t* bt, const int32_t* row_req, const int32_t* row_len,
                               const int32_t* blocks, int num_blocks, float* scores, int width,
                               int num_heads, int head_dim, int page_shift, int max_pages,
-                              hipStream_t stream) {
+                              int score_row0, hipStream_t stream) {
   const int chunk = 256;
   const int chunks = (width + chunk - 1) / chunk;
   const int total = num_blocks * chunks;
 #define DSA_IDX_F32(DI)                                                                       \
   hipLaunchKernelGGL((indexer_f32_kernel<DI>), dim3(total), dim3(kIdxThreads), 0, stream, q_idx, \
                      w, kcache, bt, row_req, row_len, blocks, scores, width, num_heads,        \
-                     page_shift, max_pages, chunk, chunks, total)
+                     page_shift, max_pages, chunk, chunks, total, score_row0)
   if (head_dim == 32) DSA_IDX_F32(32);
   else if (head_dim == 64) DSA_IDX_F32(64);
   else if (head_dim == 128) DSA_IDX_F32(128);

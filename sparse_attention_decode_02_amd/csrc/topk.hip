@@ -434,17 +434,20 @@ hipError_t launch_topk(const float* scores, const int32_t* row_len, int rows, in
 
 int topk_segments(int width, int seg) { return (width + seg - 1) / seg; }
 
-int topk_suggest_chunk(int rows, int width, int k) {
+int topk_suggest_chunk(int rows, int width, int k, bool full) {
   // One workgroup holds up to 64K keys of a row in registers; longer rows
   // re-read their chunks on every radix pass, so from there the two-stage
-  // selection over 32768-position segments is faster as long as its first
-  // stage stays within a few workgroups per compute unit.
+  // selection over 32768-position segments is faster -- for rows that fill
+  // the width (`full`) at any batch size, otherwise (a few long rows among
+  // short ones) as long as its first stage stays within a few workgroups per
+  // compute unit.
   constexpr int kSeg = kTopkThreads * 32;
   int dev = 0, cus = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
     cus = 256;
   if (width <= kTopkThreads * 64 || k > kSeg) return 0;
+  if (full) return kSeg;
   const long long wgs = (long long)rows * topk_segments(width, kSeg);
   return wgs <= 4LL * cus ? kSeg : 0;
 }

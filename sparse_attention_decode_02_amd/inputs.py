@@ -123,6 +123,15 @@ def long_context(seed: int = 20260006) -> Workload:
     return Workload("decode_b64_ctx200k_bf16", "bf16", 64, 64, 8, 128, 64, 128, 2048, prior, new, seed)
 
 
+def prefill_1m(seed: int = 20260007) -> Workload:
+    """A 2048-token prefill chunk at 1M context: one request whose cache
+    already holds 1048576 - 2048 tokens appends 2048 rows (causal lengths up
+    to 1048576) -- the case whose full score buffer takes 8 GiB, the pages'
+    reason for scoring in row windows; headline shapes otherwise."""
+    return Workload("prefill_2048_ctx1m_bf16", "bf16", 64, 64, 8, 128, 64, 128, 2048,
+                    (1048576 - 2048,), (2048,), seed)
+
+
 def ragged_lengths(seed: int, batch: int = 64, lo_frac_rows: int = 6) -> list:
     """Context lengths for the ragged batch.
 
@@ -173,6 +182,7 @@ WORKLOADS = {
     "decode": decode,
     "headline": headline,
     "long": long_context,
+    "prefill_1m": prefill_1m,
     "ragged": ragged,
     "mixed": mixed,
 }

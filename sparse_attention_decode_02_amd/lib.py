@@ -44,9 +44,9 @@ _SIGS = {
     "dsa_topk": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "dsa_topk_chunked": (_I, [_P, _P, _I, _I, _I, _I, _P, _LL, _P, _P]),
     "dsa_topk_chunked_slots": (_I, [_I, _I, _I, _I, ctypes.POINTER(_LL)]),
-    "dsa_topk_chunk_suggest": (_I, [_I, _I, _I, ctypes.POINTER(_I)]),
-    "dsa_indexer_topk_windowed": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I,
-                                       _P, _LL, _I, _P, _LL, _P, _P]),
+    "dsa_topk_chunk_suggest": (_I, [_I, _I, _I, _LL, ctypes.POINTER(_I)]),
+    "dsa_indexer_topk_windowed": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
+                                       _I, _I, _P, _LL, _I, _P, _LL, _P, _P]),
     "dsa_select_window_rows": (_I, [_I, _LL, ctypes.POINTER(_I)]),
     "dsa_read_probe": (_I, [_P, _LL, _P, _I, _P]),
     "dsa_sparse_attn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I, _P]),
@@ -116,10 +116,10 @@ class Prepared:
     stream, a raw hipStream_t as int, or None for torch's current stream)
     launches it. The tensors it was built from must stay alive and in place."""
 
-    __slots__ = ("name", "fn", "args")
+    __slots__ = ("name", "fn", "args", "keep")
 
     def __init__(self, name, fn, args):
-        self.name, self.fn, self.args = name, fn, tuple(args)
+        self.name, self.fn, self.args, self.keep = name, fn, tuple(args), None
 
     def __call__(self, stream=None):
         status = self.fn(*self.args, _stream(stream))
@@ -234,11 +234,12 @@ def topk_chunked(scores, row_len, k, chunk, cand, idx, stream=None, prepare=Fals
     return p if prepare else idx
 
 
-def topk_chunk_suggest(rows, width, k) -> int:
-    """dsa_topk_chunk_suggest: segment length for dsa_topk_chunked, or 0 for dsa_topk."""
+def topk_chunk_suggest(rows, width, k, total_keys=0) -> int:
+    """dsa_topk_chunk_suggest: segment length for dsa_topk_chunked, or 0 for
+    dsa_topk (total_keys: the sum of the row lengths, 0 if unknown)."""
     out = _I(0)
     _check("dsa_topk_chunk_suggest", _lib.dsa_topk_chunk_suggest(
-        int(rows), int(width), int(k), ctypes.byref(out)))
+        int(rows), int(width), int(k), int(total_keys), ctypes.byref(out)))
     return out.value
 
 
@@ -252,21 +253,34 @@ def select_window_rows(width, score_buffer_bytes) -> int:
 
 def indexer_topk_windowed(q_idx, w, k_idx_cache, block_table, row_req, row_len, width, page_size,
                           k, score_buffer, idx, topk_chunk=0, cand=None, stream=None,
-                          prepare=False):
+                          prepare=False, blocks=None, blocks_host=None):
     """dsa_indexer_topk_windowed: scores and top-k of every row, a window of
     rows at a time through score_buffer (any float32 device tensor; its byte
-    size sets the window); writes idx [rows][k] in place."""
+    size sets the window); optional score blocks as a device tensor plus the
+    same plan on the host (NumPy); writes idx [rows][k] in place."""
+    import numpy as np
+    nb = 0
+    bh = None
+    if blocks is not None:
+        bh = np.ascontiguousarray(np.asarray(blocks_host, dtype=np.int32))
+        nb = int(bh.shape[0])
+        if tuple(blocks.shape) != tuple(bh.shape):
+            raise ValueError("blocks and blocks_host differ")
     rows, heads, dim = q_idx.shape
     if k_idx_cache.dtype != q_idx.dtype:
         raise TypeError("q_idx and k_idx_cache dtypes differ")
     p = _call("dsa_indexer_topk_windowed", [
         _dev(q_idx, "q_idx"), _dev(w, "w", torch.float32), _dev(k_idx_cache, "k_idx_cache"),
         _dev(block_table, "block_table", torch.int32), _dev(row_req, "row_req", torch.int32),
-        _dev(row_len, "row_len", torch.int32), rows, int(width), heads, dim, int(page_size),
+        _dev(row_len, "row_len", torch.int32), None if bh is None else bh.ctypes.data,
+        None if blocks is None else _dev(blocks, "blocks", torch.int32), nb,
+        rows, int(width), heads, dim, int(page_size),
         int(block_table.shape[1]), _dtype_code(q_idx), int(k),
         _dev(score_buffer, "score_buffer", torch.float32), int(score_buffer.numel()) * 4,
         int(topk_chunk), None if cand is None else _dev(cand, "cand", torch.int32),
         0 if cand is None else int(cand.numel()), _dev(idx, "idx", torch.int32)], stream, prepare)
+    if prepare:
+        p.keep = bh  # the host plan must outlive the prepared call
     return p if prepare else idx
 
 

@@ -44,9 +44,10 @@ class DsaStep:
         self.total_keys = int(ln.astype("int64").sum())  # the indexer's scheduling hint
         self.row_req = torch.from_numpy(req).to(dev)
         self.row_len = torch.from_numpy(ln).to(dev)
-        self.blocks = None
+        self.blocks = self.blocks_host = None
         if block_rows > 1:
-            self.blocks = torch.from_numpy(lib.plan_blocks(req, block_rows)).to(dev)
+            self.blocks_host = lib.plan_blocks(req, block_rows)
+            self.blocks = torch.from_numpy(self.blocks_host).to(dev)
         shape = (self.rows, wl.hq, wl.hkv, wl.d, wl.topk, inp.q.dtype)
         if fused is None:
             s = num_splits or lib.sparse_attn_splits(*shape)
@@ -57,11 +58,11 @@ class DsaStep:
         # Score rows held at once: all of them, or a window that fits the buffer.
         self.window_rows = self.rows
         if score_buffer_bytes is not None:
-            if block_rows > 1:
-                raise ValueError("score windows take no score blocks")
             self.window_rows = min(self.rows, lib.select_window_rows(self.width, score_buffer_bytes))
         if topk_chunk is None:
-            topk_chunk = lib.topk_chunk_suggest(self.window_rows, self.width, wl.topk)
+            # The suggestion for a window's rows, at the batch's fill.
+            window_keys = self.total_keys * self.window_rows // max(1, self.rows)
+            topk_chunk = lib.topk_chunk_suggest(self.window_rows, self.width, wl.topk, window_keys)
         self.topk_chunk = topk_chunk
         self.windowed = score_buffer_bytes is not None
         self.scores = torch.empty(self.window_rows, self.width, dtype=torch.float32, device=dev)
@@ -91,7 +92,7 @@ class DsaStep:
             self._calls["indexer"] = lib.indexer_topk_windowed(
                 i.qI, i.w, i.kI_cache, i.block_table, self.row_req, self.row_len, self.width,
                 wl.page, wl.topk, self.scores, self.idx, topk_chunk=self.topk_chunk,
-                cand=self.cand, prepare=True)
+                cand=self.cand, prepare=True, blocks=self.blocks, blocks_host=self.blocks_host)
         else:
             self._calls["indexer"] = lib.indexer_scores(
                 i.qI, i.w, i.kI_cache, i.block_table, self.row_req, self.row_len, self.scores,

@@ -195,6 +195,36 @@ def test_topk_chunked_slots():
         lib.topk_chunked_slots(4, 128, 16, 8)
 
 
+@pytest.mark.parametrize("plan,code", [
+    ([(0, 2), (2, 2)], OK), ([(0, 1), (1, 3)], WS), ([(0, 2), (3, 1)], SHAPE),
+    ([(0, 2), (2, 1)], SHAPE), ([(0, 0), (0, 4)], SHAPE), ([(1, 3)], SHAPE),
+])
+def test_windowed_block_plan(plan, code):
+    """A block plan must cover the rows in order; a block longer than the
+    window (2 rows here) cannot be placed. Every status is decided on the
+    host before any launch; a valid plan is shown by the next check failing
+    instead (an unsupported head dim), so the fake pointers are never used."""
+    import numpy as np
+    bh = np.asarray(plan, np.int32)
+    args = _windowed_args(blocks_host=bh.ctypes.data, blocks_dev=A, num_blocks=len(plan))
+    st = lib._lib.dsa_indexer_topk_windowed(*args)
+    if code == OK:
+        args = _windowed_args(blocks_host=bh.ctypes.data, blocks_dev=A, num_blocks=len(plan),
+                              head_dim=96)
+        assert lib._lib.dsa_indexer_topk_windowed(*args) == UNSUP
+    else:
+        assert st == code
+
+
+def test_topk_chunk_suggest():
+    assert lib.topk_chunk_suggest(64, 32768, 2048, 64 * 32768) == 0  # rows fit a workgroup
+    assert lib.topk_chunk_suggest(2048, 1 << 20, 2048, 2048 << 20) == 32768  # full long rows
+    assert lib.topk_chunk_suggest(2048, 1 << 17, 2048, 2048 * 9000) == 0  # mostly short rows
+    out = ctypes.c_int(0)
+    assert lib._lib.dsa_topk_chunk_suggest(4, 128, 16, -1, ctypes.byref(out)) == SHAPE
+    assert lib._lib.dsa_topk_chunk_suggest(4, 128, 16, 4 * 128 + 1, ctypes.byref(out)) == SHAPE
+
+
 def test_select_window_rows():
     assert lib.select_window_rows(128, 128 * 4 * 3 + 5) == 3
     assert lib.select_window_rows(32768, 1 << 30) == 8192
@@ -213,7 +243,8 @@ def test_read_probe_rejects(args, code):
 
 
 def _windowed_args(**kw):
-    a = dict(q_idx=A, w=A, k_idx_cache=A, block_table=A, row_req=A, row_len=A, rows=4, width=128,
+    a = dict(q_idx=A, w=A, k_idx_cache=A, block_table=A, row_req=A, row_len=A, blocks_host=None,
+             blocks_dev=None, num_blocks=0, rows=4, width=128,
              num_heads=64, head_dim=128, page_size=64, max_pages=8, dtype=1, k=16, score_buffer=A,
              score_buffer_bytes=128 * 4 * 2, topk_chunk=0, cand=None, cand_slots=0, idx=A,
              stream=None)
@@ -227,6 +258,7 @@ def _windowed_args(**kw):
     (dict(topk_chunk=32, cand=A, cand_slots=2 * 2 * 4 * 16 - 1), WS), (dict(topk_chunk=8, cand=A, cand_slots=999), SHAPE),
     (dict(k=0), SHAPE), (dict(head_dim=96), UNSUP), (dict(score_buffer=A + 4), ALIGN),
     (dict(page_size=48), SHAPE), (dict(rows=-1), SHAPE), (dict(rows=0), OK),
+    (dict(num_blocks=2), NULL), (dict(num_blocks=-1), SHAPE),
 ])
 def test_windowed_rejects(kw, code):
     assert lib._lib.dsa_indexer_topk_windowed(*_windowed_args(**kw)) == code

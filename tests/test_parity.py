@@ -275,8 +275,11 @@ def test_windowed_matches_full_batch(window_rows, topk_chunk):
 
 @pytest.mark.parametrize("kw", [dict(topk_chunk=1024), dict(score_buffer_bytes=6 * 5120 * 4),
                                 dict(score_buffer_bytes=6 * 5120 * 4, topk_chunk=512),
-                                dict(topk_chunk=None)],
-                         ids=["chunked", "windowed", "windowed-chunked", "suggested"])
+                                dict(topk_chunk=None),
+                                dict(score_buffer_bytes=16 * 5120 * 4, block_rows=8),
+                                dict(score_buffer_bytes=9 * 5120 * 4, block_rows=4, topk_chunk=512)],
+                         ids=["chunked", "windowed", "windowed-chunked", "suggested",
+                              "windowed-blocks", "windowed-blocks-chunked"])
 def test_step_variants_bit_identical(kw):
     """The step with the two-stage top-k and/or score windows gives the
     default step's indices and outputs bit for bit."""
@@ -447,11 +450,13 @@ def _same_selection_other_ways(step):
     torch.cuda.synchronize()
     assert torch.equal(idx, step.idx), "two-stage top-k differs"
     del cand
-    window = 7
+    # Windows of 16 rows over the step's score blocks (at most 8 rows each).
+    window = 16
     buf = torch.empty(window * step.width, dtype=torch.float32, device="cuda")
     idx.fill_(-7)
     lib.indexer_topk_windowed(inp.qI, inp.w, inp.kI_cache, inp.block_table, step.row_req,
-                              step.row_len, step.width, wl.page, wl.topk, buf, idx)
+                              step.row_len, step.width, wl.page, wl.topk, buf, idx,
+                              blocks=step.blocks, blocks_host=step.blocks_host)
     torch.cuda.synchronize()
     assert torch.equal(idx, step.idx), "windowed indexer + top-k differs"
     _say(f"  two-stage top-k (chunk {chunk}) and {window}-row windows: identical indices")
@@ -477,6 +482,12 @@ def _full(wl, rows_fn):
 
 def test_headline_full_size():
     _full(I.headline(), lambda s: [0, 1, 37, s.rows - 1])
+
+
+def test_prefill_1m_full_size():
+    """A 2048-token prefill chunk at 1M context (8 GiB of scores at once), in
+    the bench's configuration, then checked as every full-size workload is."""
+    _full(I.prefill_1m(), lambda s: [0, s.rows - 1])
 
 
 def test_long_context_full_size():
