@@ -5,6 +5,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 #include "../../include/dsa.h"
 #include "dsa_kernels.h"
 
@@ -56,8 +58,10 @@ int indexer_check(const void* q_idx, const float* w, const void* k_idx_cache,
     return DSA_ERR_ALIGN;
   const int nb = blocks ? num_blocks : rows;
   if (rows > 0 && dtype == DSA_BF16) {
-    const int chunk = dsa::indexer_chunk_keys(nb, width, num_heads, head_dim, full);
-    if ((long long)nb * ((width + chunk - 1) / chunk) > INT32_MAX) return DSA_ERR_SHAPE;
+    int chunk = dsa::indexer_chunk_keys(nb, width, num_heads, head_dim, full);
+    if (blocks && dsa::indexer_uses_blocks(rows, nb))
+      chunk = std::min(chunk, dsa::indexer_block_chunk_keys(nb, width, num_heads, head_dim, full));
+    if ((long long)nb * ((width + chunk - 1) / chunk) > INT32_MAX - 64) return DSA_ERR_SHAPE;
   } else if (rows > 0 && (long long)nb * ((width + 255) / 256) > INT32_MAX) {
     return DSA_ERR_SHAPE;
   }
@@ -74,8 +78,8 @@ hipError_t indexer_launch(const void* q_idx, const float* w, const void* k_idx_c
   const int nb = blocks ? num_blocks : rows;
   if (dtype == DSA_BF16)
     return dsa::launch_indexer_bf16(q_idx, w, k_idx_cache, block_table, row_req, row_len, blocks,
-                                    nb, scores, width, num_heads, head_dim, page_shift, max_pages,
-                                    full, score_row0, st);
+                                    nb, rows, scores, width, num_heads, head_dim, page_shift,
+                                    max_pages, full, score_row0, st);
   return dsa::launch_indexer_f32(static_cast<const float*>(q_idx), w,
                                  static_cast<const float*>(k_idx_cache), block_table, row_req,
                                  row_len, blocks, nb, scores, width, num_heads, head_dim,

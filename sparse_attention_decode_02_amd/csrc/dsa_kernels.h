@@ -14,17 +14,24 @@ namespace dsa {
 int device_capacity(const void* kernel, int block);
 
 // Keys a workgroup of the bf16 indexer covers for one row (a multiple of 64):
-// the chunks of all blocks fill the device about once, at most 4096 keys.
+// the chunks of all blocks fill the device about once, at most 2048 keys.
 int indexer_chunk_keys(int num_blocks, int width, int num_heads, int head_dim, bool full);
 
 // Splits of the k slots that fill the device with attention waves about once.
 int attn_default_splits(int rows, int hq, int hkv, int d, int k, bool bf16);
 
+// Whether launch_indexer_bf16 scores the blocks of several rows with the
+// block kernel (query blocks in registers, keys shared through LDS); blocks
+// of one row then go to the row kernel, launched after it.
+bool indexer_uses_blocks(int rows, int num_blocks);
+// Keys a workgroup of the block kernel covers (a multiple of 128, at most 8192).
+int indexer_block_chunk_keys(int num_blocks, int width, int num_heads, int head_dim, bool full);
+
 hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kcache,
                                const int32_t* bt, const int32_t* row_req, const int32_t* row_len,
-                               const int32_t* blocks, int num_blocks, float* scores, int width,
-                               int num_heads, int head_dim, int page_shift, int max_pages,
-                               bool full, int score_row0, hipStream_t stream);
+                               const int32_t* blocks, int num_blocks, int rows, float* scores,
+                               int width, int num_heads, int head_dim, int page_shift,
+                               int max_pages, bool full, int score_row0, hipStream_t stream);
 
 hipError_t launch_indexer_f32(const float* q_idx, const float* w, const float* kcache,
                               const int32_t* bt, const int32_t* row_req, const int32_t* row_len,

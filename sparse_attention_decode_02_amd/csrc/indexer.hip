@@ -20,11 +20,15 @@
 //
 // fp32 path (VALU): one thread per key, fp32 FMA, queries in LDS.
 //
-// Work: a workgroup takes (score block, key chunk); the rows of a block
-// belong to one request and are scored one after another against the same
-// chunk, so the chunk's keys are re-read from cache, not HBM. Chunks past a
-// row's length exit at once, so the launch depends only on (blocks, width)
-// while the work follows the real lengths.
+// Work: a workgroup takes (score block, key chunk). Chunks past a row's
+// length exit at once, so the launch depends only on (blocks, width) while
+// the work follows the real lengths. On the bf16 path, blocks of one row
+// (decode) go to the row kernel described above, whose waves stream keys
+// through registers; blocks of several rows of one request (prefill) go to
+// the block kernel, whose
+// workgroup stages each key tile once in LDS for all its rows, so a chunk's
+// keys cross HBM/L2 once per block rather than once per row and the
+// contraction runs on the matrix cores at prefill's arithmetic intensity.
 
 #include "dsa_kernels.h"
 
@@ -37,6 +41,20 @@ constexpr int kIdxThreads = 256;  // 4 waves
 constexpr int kTileKeys = 16;     // keys per MFMA tile (N of 16x16x32)
 constexpr int kKeyBufs = 3;       // key tiles per wave: 2 in flight + 1 on the matrix cores
 constexpr int kMaxChunkKeys = 2048;  // keys per workgroup chunk, at most (scores staged in LDS)
+
+// Workgroup -> item: items in groups of G are dealt round-robin to the 8
+// XCDs (workgroup i runs on XCD i % 8), so the items of a group share their
+// XCD's L2 while work that clusters in one range of items (short causal rows
+// in the low chunks, a few long rows at the end of the batch) still spreads
+// over every XCD. The grid is padded to a multiple of 8 * G; items past the
+// end exit.
+template <int G>
+__device__ __forceinline__ int xcd_grouped(int wg) {
+  const int x = wg & 7, j = wg >> 3;
+  return ((j / G) * 8 + x) * G + j % G;
+}
+
+inline int xcd_grouped_grid(int total, int G) { return (total + 8 * G - 1) / (8 * G) * (8 * G); }
 
 // max(x, 0) as a signed-integer max of the bits: one VALU op, -0.0 -> +0.0.
 __device__ __forceinline__ float relu(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
@@ -61,7 +79,7 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_mfma_kernel(
     const uint16_t* __restrict__ kc, const int32_t* __restrict__ bt,
     const int32_t* __restrict__ row_req, const int32_t* __restrict__ row_len,
     const int32_t* __restrict__ blocks, float* __restrict__ scores, int width, int page_shift,
-    int max_pages, int chunk_keys, int chunks, int total, int score_row0) {
+    int max_pages, int chunk_keys, int chunks, int total, int score_row0, int single_only) {
   constexpr int H = HT * 16;
   constexpr int KS = DI / 32;  // MFMA steps per head tile
   constexpr int QST = DI + 8;  // padded LDS row (elements): the 16 rows read together hit distinct banks
@@ -69,13 +87,19 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_mfma_kernel(
   __shared__ __attribute__((aligned(16))) float w_lds[H];
   __shared__ __attribute__((aligned(16))) float s_lds[kMaxChunkKeys];  // the chunk's scores
 
-  const int item = xcd_contiguous(blockIdx.x, total);
+  // Beside the block kernel only some blocks are this kernel's, so its
+  // items are dealt round-robin over the XCDs; alone, consecutive items
+  // (the chunks of a row) share an XCD, which measures faster for ragged
+  // batches.
+  const int item = single_only ? xcd_grouped<2>(blockIdx.x) : xcd_contiguous(blockIdx.x, total);
+  if (item >= total) return;
   const int b = item / chunks;
   const int chunk0 = (item - b * chunks) * chunk_keys;
   int first = b, nrows = 1;
   if (blocks) {
     first = blocks[2 * b];
     nrows = blocks[2 * b + 1];
+    if (single_only && nrows > 1) return;  // the block kernel's
   }
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -195,6 +219,164 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_mfma_kernel(
   }
 }
 
+// Score blocks of several rows (prefill): the roles of the row kernel are
+// swapped so that a chunk's keys cross HBM/L2 once per block instead of once
+// per row. Wave w of the 8-wave workgroup holds one row's query block in
+// registers as MFMA A fragments (HT*KS fragments of 8 bf16); the workgroup
+// stages the chunk's keys 128 at a time in LDS (rows padded to DI + 8
+// elements, so the 16 keys of a B fragment read hit distinct banks) and every
+// row of the block reads its B fragments there. Each wave scores its row's
+// tiles in the same MFMA order and with the same fp32 epilogue as the row
+// kernel, so the scores are the same bits. The rows of a block share a
+// request (the block plan's contract), so one block-table row serves all of
+// them; its entries for the chunk are read once into LDS.
+//
+// Blocks of 2 <= R < 8 rows give each row 8 / R waves, which split the
+// stage's tiles; blocks of more than 8 rows are scored 8 rows at a time.
+// Blocks of one row are left to the row kernel, launched beside this one.
+constexpr int kBlkThreads = 512;                       // 8 waves
+constexpr int kBlkWaves = kBlkThreads / 64;
+constexpr int kStageKeys = 128;                        // keys per LDS stage (8 tiles)
+constexpr int kStageTiles = kStageKeys / kTileKeys;
+constexpr int kMaxBlkChunk = 8192;                     // keys per workgroup chunk, at most
+constexpr int kMinBlkChunk = 512;
+constexpr int kBlkGroup = 8;  // consecutive (chunk, block) items an XCD takes together
+
+template <int HT, int DI>
+__global__ __launch_bounds__(kBlkThreads, 4) void indexer_block_kernel(
+    const uint16_t* __restrict__ qI, const float* __restrict__ w,
+    const uint16_t* __restrict__ kc, const int32_t* __restrict__ bt,
+    const int32_t* __restrict__ row_req, const int32_t* __restrict__ row_len,
+    const int32_t* __restrict__ blocks, float* __restrict__ scores, int width, int page_shift,
+    int max_pages, int chunk_keys, int num_blocks, int total, int score_row0) {
+  constexpr int H = HT * 16;
+  constexpr int KS = DI / 32;
+  constexpr int KST = DI + 8;                          // padded LDS key row (elements)
+  constexpr int CPK = DI / 8;                          // 16-byte pieces of a key row
+  constexpr int SV = kStageKeys * CPK / kBlkThreads;   // pieces per thread per stage
+  static_assert(SV * kBlkThreads == kStageKeys * CPK, "stage must split evenly over the threads");
+  __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kStageKeys * KST];
+  __shared__ int pg_lds[kMaxBlkChunk / 16 + 1];
+  __shared__ __attribute__((aligned(16))) float w_lds[kBlkWaves][H];  // each wave's row weights
+
+  // Chunk-major order, so that the blocks of a group share a chunk.
+  const int item = xcd_grouped<kBlkGroup>(blockIdx.x);
+  if (item >= total) return;
+  const int ci = item / num_blocks;
+  const int b = item - ci * num_blocks;
+  const int chunk0 = ci * chunk_keys;
+  const int first = blocks[2 * b], nrows = blocks[2 * b + 1];
+  if (nrows < 2) return;  // the row kernel's
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
+  const int kl = lane & 15, grp = lane >> 4;
+  const int page_mask = (1 << page_shift) - 1;
+  const int32_t* btr = bt + (size_t)row_req[first] * max_pages;
+
+  for (int g0 = 0; g0 < nrows; g0 += kBlkWaves) {
+    const int R = min(nrows - g0, kBlkWaves);
+    int lmax = 0;
+    for (int i = 0; i < R; ++i) lmax = max(lmax, row_len[first + g0 + i]);
+    if (chunk0 >= lmax) continue;  // uniform over the workgroup
+    const int end = min(lmax, chunk0 + chunk_keys);
+    const int P = kBlkWaves / R;  // waves per row
+    const int sub = wv / R;
+    const bool active = sub < P;
+    const int r = first + g0 + (wv - sub * R);
+    const int L = active ? row_len[r] : 0;
+    float* out = scores + (size_t)(r - score_row0) * width;
+
+    const int p0 = chunk0 >> page_shift;
+    const int np = ((end - 1) >> page_shift) - p0 + 1;
+    __syncthreads();  // the previous group is done with pg_lds and k_lds
+    for (int i = tid; i < np; i += kBlkThreads) pg_lds[i] = btr[p0 + i];
+
+    // The head weights stay in LDS (read per tile) to leave registers for
+    // two workgroups per compute unit.
+    bf16x8 qf[HT][KS];
+    if (active) {
+      const uint16_t* qrow = qI + (size_t)r * H * DI + kl * DI + grp * 8;
+#pragma unroll
+      for (int t = 0; t < HT; ++t) {
+#pragma unroll
+        for (int kk = 0; kk < KS; ++kk)
+          qf[t][kk] = *reinterpret_cast<const bf16x8*>(qrow + t * 16 * DI + kk * 32);
+      }
+      if (lane < H) w_lds[wv][lane] = w[(size_t)r * H + lane];
+    }
+    __syncthreads();  // pg_lds and w_lds are filled
+
+    // Stage loads: 16 consecutive threads read one key's row; positions past
+    // the group's end re-read its last key (valid, never stored).
+    uint4 pre[SV];
+    auto fetch = [&](int st) {
+      const int s0 = chunk0 + st * kStageKeys;
+#pragma unroll
+      for (int i = 0; i < SV; ++i) {
+        const int e = tid + i * kBlkThreads;
+        const int key = e / CPK, c = e - key * CPK;
+        const int s = min(s0 + key, end - 1);
+        const int page = pg_lds[(s >> page_shift) - p0];
+        const size_t krow = ((size_t)page << page_shift) | (size_t)(s & page_mask);
+        pre[i] = *reinterpret_cast<const uint4*>(kc + krow * DI + c * 8);
+      }
+    };
+    auto stash = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < SV; ++i) {
+        const int e = tid + i * kBlkThreads;
+        const int key = e / CPK, c = e - key * CPK;
+        *reinterpret_cast<uint4*>(&k_lds[buf][key * KST + c * 8]) = pre[i];
+      }
+    };
+
+    // Blocks that share the chunk start at different stages, so that the
+    // workgroups reading it at once spread over its cache lines.
+    const int nst = (end - chunk0 + kStageKeys - 1) / kStageKeys;
+    const int rot = b % nst;
+    auto stage = [&](int i) { return i + rot < nst ? i + rot : i + rot - nst; };
+    fetch(stage(0));
+    stash(0);
+    __syncthreads();
+    for (int st = 0; st < nst; ++st) {
+      if (st + 1 < nst) fetch(stage(st + 1));
+      if (active) {
+        const uint16_t* kb = &k_lds[st & 1][kl * KST + grp * 8];
+        const int s0 = chunk0 + stage(st) * kStageKeys;
+        for (int tt = sub; tt < kStageTiles; tt += P) {
+          const int base = s0 + tt * kTileKeys;
+          if (base >= L) break;  // wave-uniform; tiles ascend within a stage
+          f32x4 acc[HT];
+#pragma unroll
+          for (int t = 0; t < HT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+          for (int kk = 0; kk < KS; ++kk) {
+            const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + tt * kTileKeys * KST + kk * 32);
+#pragma unroll
+            for (int t = 0; t < HT; ++t)
+              acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[t][kk], kf, acc[t], 0, 0, 0);
+          }
+          float part = 0.0f;
+#pragma unroll
+          for (int t = 0; t < HT; ++t) {
+            const float4 wr = *reinterpret_cast<const float4*>(&w_lds[wv][t * 16 + grp * 4]);
+            part = fmaf(wr.x, relu(acc[t][0]), part);
+            part = fmaf(wr.y, relu(acc[t][1]), part);
+            part = fmaf(wr.z, relu(acc[t][2]), part);
+            part = fmaf(wr.w, relu(acc[t][3]), part);
+          }
+          part = sum_rows(part);
+          const int s = base + kl;
+          if (grp == 0 && s < L) out[s] = part + 0.0f;
+        }
+      }
+      if (st + 1 < nst) stash((st + 1) & 1);
+      __syncthreads();
+    }
+  }
+}
+
 template <int DI>
 __global__ __launch_bounds__(kIdxThreads) void indexer_f32_kernel(
     const float* __restrict__ qI, const float* __restrict__ w, const float* __restrict__ kc,
@@ -284,20 +466,67 @@ int indexer_chunk_keys(int num_blocks, int width, int num_heads, int head_dim, b
   return max(256, min(max_chunk, chunk));
 }
 
+static const void* indexer_block_kernel_ptr(int num_heads, int head_dim) {
+  if (num_heads == 64 && head_dim == 128) return (const void*)indexer_block_kernel<4, 128>;
+  if (num_heads == 32 && head_dim == 128) return (const void*)indexer_block_kernel<2, 128>;
+  if (num_heads == 64 && head_dim == 64) return (const void*)indexer_block_kernel<4, 64>;
+  if (num_heads == 32 && head_dim == 64) return (const void*)indexer_block_kernel<2, 64>;
+  return nullptr;
+}
+
+bool indexer_uses_blocks(int rows, int num_blocks) {
+  // Some block holds more than one row (the row counts are on the device).
+  return num_blocks > 0 && rows > num_blocks;
+}
+
+int indexer_block_chunk_keys(int num_blocks, int width, int num_heads, int head_dim, bool full) {
+  // As for the row kernel: about one round of workgroups over the device,
+  // in whole stages; 2048 keys at most unless the rows fill the width (causal
+  // prefill blocks of unequal length then balance over more chunks).
+  const void* kern = indexer_block_kernel_ptr(num_heads, head_dim);
+  int cap = kern ? device_capacity(kern, kBlkThreads) : 0;
+  if (cap <= 0) cap = 256;
+  const int per_block = max(1, cap / max(1, num_blocks));
+  int chunk = (width + per_block - 1) / per_block;
+  chunk = ((chunk + kStageKeys - 1) / kStageKeys) * kStageKeys;
+  return max(kMinBlkChunk, min(full ? kMaxBlkChunk : 2048, chunk));
+}
+
 hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kcache,
                                const int32_t* bt, const int32_t* row_req, const int32_t* row_len,
-                               const int32_t* blocks, int num_blocks, float* scores, int width,
-                               int num_heads, int head_dim, int page_shift, int max_pages,
-                               bool full, int score_row0, hipStream_t stream) {
+                               const int32_t* blocks, int num_blocks, int rows, float* scores,
+                               int width, int num_heads, int head_dim, int page_shift,
+                               int max_pages, bool full, int score_row0, hipStream_t stream) {
+  const auto* q = static_cast<const uint16_t*>(q_idx);
+  const auto* k = static_cast<const uint16_t*>(kcache);
+  const bool with_block_kernel = blocks && indexer_uses_blocks(rows, num_blocks);
+  if (with_block_kernel) {
+    const int chunk = indexer_block_chunk_keys(num_blocks, width, num_heads, head_dim, full);
+    const int total = num_blocks * ((width + chunk - 1) / chunk);
+    const int grid = xcd_grouped_grid(total, kBlkGroup);
+#define DSA_IDX_BLK(HT, DI)                                                                    \
+  hipLaunchKernelGGL((indexer_block_kernel<HT, DI>), dim3(grid), dim3(kBlkThreads), 0, stream,  \
+                     q, w, k, bt, row_req, row_len, blocks, scores, width, page_shift,          \
+                     max_pages, chunk, num_blocks, total, score_row0)
+    if (num_heads == 64 && head_dim == 128) DSA_IDX_BLK(4, 128);
+    else if (num_heads == 32 && head_dim == 128) DSA_IDX_BLK(2, 128);
+    else if (num_heads == 64 && head_dim == 64) DSA_IDX_BLK(4, 64);
+    else if (num_heads == 32 && head_dim == 64) DSA_IDX_BLK(2, 64);
+    else return hipErrorInvalidValue;
+#undef DSA_IDX_BLK
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  const int single_only = with_block_kernel ? 1 : 0;
   const int chunk = indexer_chunk_keys(num_blocks, width, num_heads, head_dim, full);
   const int chunks = (width + chunk - 1) / chunk;
   const int total = num_blocks * chunks;
-  const auto* q = static_cast<const uint16_t*>(q_idx);
-  const auto* k = static_cast<const uint16_t*>(kcache);
 #define DSA_IDX_LAUNCH(HT, DI)                                                                 \
-  hipLaunchKernelGGL((indexer_mfma_kernel<HT, DI>), dim3(total), dim3(kIdxThreads), 0, stream, \
+  hipLaunchKernelGGL((indexer_mfma_kernel<HT, DI>),                                            \
+                     dim3(single_only ? xcd_grouped_grid(total, 2) : total), dim3(kIdxThreads), 0, \
+                     stream,                                                                   \
                      q, w, k, bt, row_req, row_len, blocks, scores, width, page_shift,         \
-                     max_pages, chunk, chunks, total, score_row0)
+                     max_pages, chunk, chunks, total, score_row0, single_only)
   if (num_heads == 64 && head_dim == 128) DSA_IDX_LAUNCH(4, 128);
   else if (num_heads == 32 && head_dim == 128) DSA_IDX_LAUNCH(2, 128);
   else if (num_heads == 64 && head_dim == 64) DSA_IDX_LAUNCH(4, 64);

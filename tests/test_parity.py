@@ -341,6 +341,41 @@ def test_score_blocks_are_bit_identical():
         assert torch.equal(s.view(torch.int32), ref.view(torch.int32)), f"block_rows {br}"
 
 
+def _block_mix(hi, di, page, seed=31):
+    # Blocks of 37 (8+8+8+8+5 rows), 16, 9 (8+1) and 64 rows, and of 2, 3, 6,
+    # 7 rows (4, 2, 1, 1 waves per row) for the block kernel, and one block
+    # of one row for the row kernel launched beside it: 145 rows in 9 blocks.
+    # Lengths cross tiles, stages, pages and chunks.
+    prior = (0, 130, 1000, 5000, 62, 255, 2999, 16, 700)
+    new = (37, 16, 9, 64, 1, 2, 3, 6, 7)
+    return I.custom(I.decode(), name=f"block_mix_{hi}x{di}_p{page}", hq=16, hkv=2, hi=hi, di=di,
+                    page=page, topk=256, prior=prior, new=new, seed=seed)
+
+
+@pytest.mark.parametrize("hi,di,page", [(64, 128, 64), (32, 128, 16), (64, 64, 16), (32, 64, 64)])
+def test_block_indexer_matches_row_kernel(hi, di, page):
+    """Scores of score blocks (query blocks in registers, keys shared
+    through LDS) equal the one-row-per-block scores bit for bit, unwritten
+    positions included; rows of length 0 inside a block stay unwritten."""
+    inp = _host_inputs(_block_mix(hi, di, page))
+    ref = run_step(inp, block_rows=1)
+    blk = run_step(inp, block_rows=64)
+    _say(f"indexer {hi}x{di}, page {page}: {blk.rows} rows in {len(blk.blocks_host)} blocks")
+    assert torch.equal(blk.scores.view(torch.int32), ref.scores.view(torch.int32))
+    assert torch.equal(blk.idx, ref.idx)
+    if (hi, di, page) == (64, 128, 64):
+        _check_all(blk)
+    pad = [3, 40, 53, 100]  # inside the 37-, 16-, 9- and 64-row blocks
+    for st in (ref, blk):
+        st.row_len[pad] = 0
+        st.scores.view(torch.int32).fill_(CANARY)
+        st.run()
+    torch.cuda.synchronize()
+    assert torch.equal(blk.scores.view(torch.int32), ref.scores.view(torch.int32))
+    for r in pad:
+        assert bool((blk.scores[r].view(torch.int32) == CANARY).all())
+
+
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "two-launch"])
 def test_graph_replay_matches_eager(fused):
     """The step recorded into a HIP graph and replayed gives the eager step's
