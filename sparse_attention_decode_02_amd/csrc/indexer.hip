@@ -36,6 +36,7 @@ namespace dsa {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef unsigned u32x4 __attribute__((ext_vector_type(4)));  // a native vector (promotes to registers)
 
 constexpr int kIdxThreads = 256;  // 4 waves
 constexpr int kTileKeys = 16;     // keys per MFMA tile (N of 16x16x32)
@@ -242,6 +243,34 @@ constexpr int kMaxBlkChunk = 8192;                     // keys per workgroup chu
 constexpr int kMinBlkChunk = 512;
 constexpr int kBlkGroup = 8;  // consecutive (chunk, block) items an XCD takes together
 
+// One LDS stage of the block kernel: thread t holds pieces (key0 + i * KSTEP,
+// c0) for i < SV, with key0 = t / CPK and c0 = t % CPK (CPK 16-byte pieces
+// per key row). Positions past `end` re-read the key at end - 1. The page of
+// a position comes from pg_lds (the chunk's block-table entries from page p0).
+template <int DI, int SV>
+__device__ __forceinline__ void blk_fetch(u32x4 (&pre)[SV], const uint16_t* __restrict__ kc,
+                                          const int* pg_lds, int s0, int end, int key0, int c0,
+                                          int page_shift, int p0) {
+  constexpr int KSTEP = kBlkThreads / (DI / 8);
+  const int page_mask = (1 << page_shift) - 1;
+#pragma unroll
+  for (int i = 0; i < SV; ++i) {
+    const int s = min(s0 + key0 + i * KSTEP, end - 1);
+    const int page = pg_lds[(s >> page_shift) - p0];
+    const size_t krow = ((size_t)page << page_shift) | (size_t)(s & page_mask);
+    pre[i] = *reinterpret_cast<const u32x4*>(kc + krow * DI + c0 * 8);
+  }
+}
+
+template <int DI, int SV>
+__device__ __forceinline__ void blk_stash(const u32x4 (&pre)[SV], uint16_t* buf, int key0, int c0) {
+  constexpr int KSTEP = kBlkThreads / (DI / 8);
+  constexpr int KST = DI + 8;
+  uint16_t* dst = buf + key0 * KST + c0 * 8;
+#pragma unroll
+  for (int i = 0; i < SV; ++i) *reinterpret_cast<u32x4*>(dst + i * KSTEP * KST) = pre[i];
+}
+
 template <int HT, int DI>
 __global__ __launch_bounds__(kBlkThreads, 4) void indexer_block_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w,
@@ -271,8 +300,8 @@ __global__ __launch_bounds__(kBlkThreads, 4) void indexer_block_kernel(
   const int lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane((int)(tid >> 6));
   const int kl = lane & 15, grp = lane >> 4;
-  const int page_mask = (1 << page_shift) - 1;
   const int32_t* btr = bt + (size_t)row_req[first] * max_pages;
+  const int key0 = tid / CPK, c0 = tid - key0 * CPK;  // this thread's first stage piece
 
   for (int g0 = 0; g0 < nrows; g0 += kBlkWaves) {
     const int R = min(nrows - g0, kBlkWaves);
@@ -307,40 +336,19 @@ __global__ __launch_bounds__(kBlkThreads, 4) void indexer_block_kernel(
     }
     __syncthreads();  // pg_lds and w_lds are filled
 
-    // Stage loads: 16 consecutive threads read one key's row; positions past
+    // Stage loads: CPK consecutive threads read one key's row; positions past
     // the group's end re-read its last key (valid, never stored).
-    uint4 pre[SV];
-    auto fetch = [&](int st) {
-      const int s0 = chunk0 + st * kStageKeys;
-#pragma unroll
-      for (int i = 0; i < SV; ++i) {
-        const int e = tid + i * kBlkThreads;
-        const int key = e / CPK, c = e - key * CPK;
-        const int s = min(s0 + key, end - 1);
-        const int page = pg_lds[(s >> page_shift) - p0];
-        const size_t krow = ((size_t)page << page_shift) | (size_t)(s & page_mask);
-        pre[i] = *reinterpret_cast<const uint4*>(kc + krow * DI + c * 8);
-      }
-    };
-    auto stash = [&](int buf) {
-#pragma unroll
-      for (int i = 0; i < SV; ++i) {
-        const int e = tid + i * kBlkThreads;
-        const int key = e / CPK, c = e - key * CPK;
-        *reinterpret_cast<uint4*>(&k_lds[buf][key * KST + c * 8]) = pre[i];
-      }
-    };
-
-    // Blocks that share the chunk start at different stages, so that the
-    // workgroups reading it at once spread over its cache lines.
+    u32x4 pre[SV];
     const int nst = (end - chunk0 + kStageKeys - 1) / kStageKeys;
     const int rot = b % nst;
     auto stage = [&](int i) { return i + rot < nst ? i + rot : i + rot - nst; };
-    fetch(stage(0));
-    stash(0);
+    blk_fetch<DI, SV>(pre, kc, pg_lds, chunk0 + stage(0) * kStageKeys, end, key0, c0, page_shift, p0);
+    blk_stash<DI, SV>(pre, k_lds[0], key0, c0);
     __syncthreads();
     for (int st = 0; st < nst; ++st) {
-      if (st + 1 < nst) fetch(stage(st + 1));
+      if (st + 1 < nst)
+        blk_fetch<DI, SV>(pre, kc, pg_lds, chunk0 + stage(st + 1) * kStageKeys, end, key0, c0,
+                          page_shift, p0);
       if (active) {
         const uint16_t* kb = &k_lds[st & 1][kl * KST + grp * 8];
         const int s0 = chunk0 + stage(st) * kStageKeys;
@@ -371,7 +379,7 @@ __global__ __launch_bounds__(kBlkThreads, 4) void indexer_block_kernel(
           if (grp == 0 && s < L) out[s] = part + 0.0f;
         }
       }
-      if (st + 1 < nst) stash((st + 1) & 1);
+      if (st + 1 < nst) blk_stash<DI, SV>(pre, k_lds[(st + 1) & 1], key0, c0);
       __syncthreads();
     }
   }
