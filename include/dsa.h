@@ -176,6 +176,15 @@ int dsa_indexer_scores_total(const void* q_idx, const float* w, const void* k_id
 int dsa_topk(const float* scores, const int32_t* row_len, int rows, int width, int k,
              int32_t* idx, void* stream);
 
+/* dsa_topk with a scheduling hint: total_keys = the sum of row_len over the
+ * rows (known on the host from the row plan; 0 = unknown). Batches of many
+ * rows that are short on average run in smaller workgroups. The indices are
+ * identical either way; the launch shape depends only on the arguments, so a
+ * replayed step must pass the same hint. total_keys outside
+ * [0, rows * width]: DSA_ERR_SHAPE. */
+int dsa_topk_total(const float* scores, const int32_t* row_len, int rows, int width, int k,
+                   long long total_keys, int32_t* idx, void* stream);
+
 /* ------------------------------------------------------------------------
  * dsa_topk_chunked -- the same selection as dsa_topk, in two stages.
  *

@@ -151,6 +151,16 @@ int dsa_topk(const float* scores, const int32_t* row_len, int rows, int width, i
       dsa::launch_topk(scores, row_len, rows, width, k, idx, static_cast<hipStream_t>(stream)));
 }
 
+int dsa_topk_total(const float* scores, const int32_t* row_len, int rows, int width, int k,
+                   long long total_keys, int32_t* idx, void* stream) {
+  if (total_keys < 0 || total_keys > (long long)rows * width) return DSA_ERR_SHAPE;
+  const int st = topk_check(scores, row_len, rows, width, k, idx);
+  if (st != DSA_OK) return st;
+  if (rows == 0) return DSA_OK;
+  return launch_status(dsa::launch_topk(scores, row_len, rows, width, k, idx,
+                                        static_cast<hipStream_t>(stream), total_keys));
+}
+
 int dsa_topk_chunked_slots(int rows, int width, int k, int chunk, long long* slots) {
   if (!slots) return DSA_ERR_NULL;
   return topk_chunked_check(rows, width, k, chunk, slots);

@@ -39,8 +39,9 @@ hipError_t launch_indexer_f32(const float* q_idx, const float* w, const float* k
                               int num_heads, int head_dim, int page_shift, int max_pages,
                               int score_row0, hipStream_t stream);
 
+// total_keys: the sum of the row lengths if the host knows it, else 0.
 hipError_t launch_topk(const float* scores, const int32_t* row_len, int rows, int width, int k,
-                       int32_t* idx, hipStream_t stream);
+                       int32_t* idx, hipStream_t stream, long long total_keys = 0);
 // Segments of `seg` positions per row of `width` (the stage-1 workgroups per row).
 int topk_segments(int width, int seg);
 // Segment length for dsa_topk_chunked when it beats the one-pass kernel, else 0.

@@ -394,7 +394,7 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
 }
 
 hipError_t launch_topk(const float* scores, const int32_t* row_len, int rows, int width, int k,
-                       int32_t* idx, hipStream_t stream) {
+                       int32_t* idx, hipStream_t stream, long long total_keys) {
   // 32 keys per thread cover rows up to 32768 positions in registers. Wider
   // batches of few rows (the long rows set the kernel's time) hold 64 keys per
   // thread, which halves the chunk re-reads of rows past 32768; batches of
@@ -408,12 +408,19 @@ hipError_t launch_topk(const float* scores, const int32_t* row_len, int rows, in
   // about the same in barriers and bin scans whatever the row length, and
   // with half the waves those fixed costs halve (batch 8, width 4096:
   // 15.0 -> 7.7 us); from 32768 positions the 1024-thread kernel is faster.
+  // Batches of at least 4 rows per CU whose rows are short on average (the
+  // host's total_keys hint) take 512 x 16 whatever the width: the rows fill
+  // the device several times over, so small workgroups that many CUs hold at
+  // once beat wide ones, and the few long rows re-read their chunks (mixed
+  // prefill + decode step, 2108 rows, width 131072, mean length ~10K:
+  // 219 -> 140 us; batch 64 ragged keeps the wide kernel, 32 vs 43 us).
+  const bool many_short = total_keys > 0 && rows >= 4 * cus && total_keys <= 16384LL * rows;
   if (width <= 512 * 8) {
     hipLaunchKernelGGL((topk_kernel<512, 8>), dim3(rows), dim3(512), 0, stream, scores, row_len,
                        width, k, idx, 0, 1, nullptr);
     return hipGetLastError();
   }
-  if (width <= 512 * 16) {
+  if (width <= 512 * 16 || many_short) {
     hipLaunchKernelGGL((topk_kernel<512, 16>), dim3(rows), dim3(512), 0, stream, scores, row_len,
                        width, k, idx, 0, 1, nullptr);
     return hipGetLastError();

@@ -42,6 +42,7 @@ _SIGS = {
     "dsa_indexer_scores_total": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,
                                       _LL, _P]),
     "dsa_topk": (_I, [_P, _P, _I, _I, _I, _P, _P]),
+    "dsa_topk_total": (_I, [_P, _P, _I, _I, _I, _LL, _P, _P]),
     "dsa_topk_chunked": (_I, [_P, _P, _I, _I, _I, _I, _P, _LL, _P, _P]),
     "dsa_topk_chunked_slots": (_I, [_I, _I, _I, _I, ctypes.POINTER(_LL)]),
     "dsa_topk_chunk_suggest": (_I, [_I, _I, _I, _LL, ctypes.POINTER(_I)]),
@@ -206,12 +207,17 @@ def indexer_scores(q_idx, w, k_idx_cache, block_table, row_req, row_len, scores,
     return p if prepare else scores
 
 
-def topk(scores, row_len, k, idx, stream=None, prepare=False):
-    """dsa_topk: writes idx [rows][k] in place."""
+def topk(scores, row_len, k, idx, stream=None, total_keys=None, prepare=False):
+    """dsa_topk (dsa_topk_total when ``total_keys``, the host-known sum of the
+    row lengths, is given): writes idx [rows][k] in place."""
     rows, width = scores.shape
-    p = _call("dsa_topk", [_dev(scores, "scores", torch.float32),
-                           _dev(row_len, "row_len", torch.int32), rows, width, int(k),
-                           _dev(idx, "idx", torch.int32)], stream, prepare)
+    args = [_dev(scores, "scores", torch.float32), _dev(row_len, "row_len", torch.int32), rows,
+            width, int(k)]
+    if total_keys is None:
+        p = _call("dsa_topk", args + [_dev(idx, "idx", torch.int32)], stream, prepare)
+    else:
+        p = _call("dsa_topk_total", args + [int(total_keys), _dev(idx, "idx", torch.int32)],
+                  stream, prepare)
     return p if prepare else idx
 
 

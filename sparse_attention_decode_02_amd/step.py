@@ -103,7 +103,7 @@ class DsaStep:
                                                        prepare=True)
             else:
                 self._calls["topk"] = lib.topk(self.scores, self.row_len, wl.topk, self.idx,
-                                               prepare=True)
+                                               total_keys=self.total_keys, prepare=True)
         if self.fused:
             self._calls["attention"] = lib.sparse_attn_merged(
                 i.q, i.k_cache, i.v_cache, i.block_table, self.row_req, self.idx, wl.page,

@@ -170,6 +170,16 @@ def test_topk_rejects(kw, code):
     assert lib._lib.dsa_topk(*_topk_args(**kw)) == code
 
 
+@pytest.mark.parametrize("total,kw,code", [
+    (-1, {}, SHAPE), (4 * 128 + 1, {}, SHAPE), (4 * 128, dict(scores=None), NULL),
+    (4 * 128, dict(width=66), SHAPE), (0, dict(rows=0), OK), (4 * 128, dict(rows=0), SHAPE),
+    (4 * 128, dict(idx=A + 1), ALIGN),
+])
+def test_topk_total_rejects(total, kw, code):
+    args = _topk_args(**kw)
+    assert lib._lib.dsa_topk_total(*args[:-2], total, *args[-2:]) == code
+
+
 def _chunked_args(**kw):
     a = dict(scores=A, row_len=A, rows=4, width=128, k=16, chunk=32, cand=A, cand_slots=2 * 4 * 4 * 16,
              idx=A, stream=None)

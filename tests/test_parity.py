@@ -215,6 +215,45 @@ def test_topk_edges(k, copies, width):
         assert np.array_equal(got[i], want), f"{name}: first diff at {np.flatnonzero(got[i] != want)[:5]}"
 
 
+@pytest.mark.parametrize("k", [16, 2048])
+def test_topk_hint_many_short_rows(k):
+    """A batch of at least four rows per CU, short on average: with the
+    row-length hint the selection runs in the small-workgroup kernel whatever
+    the width; the edge rows (up to 70016 long) and sampled short rows
+    against the oracle, every row bit for bit against the unhinted call."""
+    from sparse_attention_decode_02_amd import lib
+    width = 70016
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    edge = _topk_case_rows(width, k)
+    n = max(4 * cus, 1024) + len(edge)
+    rng = np.random.default_rng(11)
+    lens = rng.integers(1, 9000, n).astype(np.int32)
+    scores = np.full((n, width), np.nan, np.float32)
+    short = rng.integers(-64, 64, (n, 9000)).astype(np.float32)  # small integers: many ties
+    for i in range(n):
+        scores[i, : lens[i]] = short[i, : lens[i]]
+    for i, (_, sc) in enumerate(edge):
+        scores[i, : len(sc)] = sc
+        scores[i, len(sc):] = np.nan
+        lens[i] = len(sc)
+    total = int(lens.astype(np.int64).sum())
+    assert n >= 4 * cus and total <= 16384 * n
+    _say(f"top-k with the hint, k {k}, {n} rows, mean length {total / n:.0f}")
+    s_d = torch.from_numpy(scores).cuda()
+    l_d = torch.from_numpy(lens).cuda()
+    plain = torch.full((n, k), -7, dtype=torch.int32, device="cuda")
+    hinted = torch.full((n, k), -7, dtype=torch.int32, device="cuda")
+    lib.topk(s_d, l_d, k, plain)
+    lib.topk(s_d, l_d, k, hinted, total_keys=total)
+    torch.cuda.synchronize()
+    assert torch.equal(hinted, plain)
+    got = hinted.cpu().numpy()
+    for i in list(range(len(edge))) + [len(edge), n // 2, n - 1]:
+        sc = scores[i, : lens[i]]
+        want = O.topk_row(sc, int(lens[i]), k)
+        assert np.array_equal(got[i], want), f"row {i}: first diff at {np.flatnonzero(got[i] != want)[:5]}"
+
+
 def _edge_batch(k):
     width = 70016
     cases = _topk_case_rows(width, k)
