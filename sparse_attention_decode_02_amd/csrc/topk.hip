@@ -367,6 +367,9 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
         ((uint32_t)popcount(gtm) << 16) | (uint32_t)popcount(eqm), scan_sh[2 + (c & 1)], &total);
     uint32_t g = gt_run + (excl >> 16);
     uint32_t e = eq_run + (excl & 0xFFFFu);
+    // The winners' keys (segment mode) are re-read from the row, a cache
+    // hit: indexing key[] by the bit found at run time would move the whole
+    // array out of registers.
     Mask m = gtm | eqm;
     while (m) {
       const int j = lowest_bit(m);
@@ -377,13 +380,13 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
         const uint32_t slot = g + min(e, need);
         if (slot < (uint32_t)k) {
           out[slot] = pos_of(base + j);
-          if constexpr (kMode == kSegment) outk[slot] = key[j];
+          if constexpr (kMode == kSegment) outk[slot] = order_key(row[base + j]);
         }
         ++g;
       } else {
         if (e < need && g + e < (uint32_t)k) {
           out[g + e] = pos_of(base + j);
-          if constexpr (kMode == kSegment) outk[g + e] = key[j];
+          if constexpr (kMode == kSegment) outk[g + e] = order_key(row[base + j]);
         }
         ++e;
       }
@@ -467,10 +470,16 @@ hipError_t launch_topk_chunked(const float* scores, const int32_t* row_len, int 
   const int nseg = topk_segments(width, seg);
   const long long wgs = (long long)rows * nseg;
   int32_t* keys = cand + (size_t)wgs * k;
-  if (seg <= kTopkThreads * 32)
-    hipLaunchKernelGGL((topk_kernel<kTopkThreads, 32, kSegment>), dim3((unsigned)wgs),
-                       dim3(kTopkThreads), 0, stream, scores, row_len, width, k, cand, seg, nseg,
-                       keys);
+  // Segments of up to 32768 positions run in 512-thread workgroups: the
+  // stage has many of them, and smaller workgroups pay less in barriers per
+  // radix pass (512 x 1M positions in 32768-position segments: 1490 ->
+  // 1200 us against 1024 threads x 32 keys).
+  if (seg <= 512 * 32)
+    hipLaunchKernelGGL((topk_kernel<512, 32, kSegment>), dim3((unsigned)wgs), dim3(512), 0,
+                       stream, scores, row_len, width, k, cand, seg, nseg, keys);
+  else if (seg <= 512 * 64)
+    hipLaunchKernelGGL((topk_kernel<512, 64, kSegment>), dim3((unsigned)wgs), dim3(512), 0,
+                       stream, scores, row_len, width, k, cand, seg, nseg, keys);
   else
     hipLaunchKernelGGL((topk_kernel<kTopkThreads, 64, kSegment>), dim3((unsigned)wgs),
                        dim3(kTopkThreads), 0, stream, scores, row_len, width, k, cand, seg, nseg,
