@@ -358,6 +358,9 @@ __global__ __launch_bounds__(kBlkThreads, 4) void indexer_block_kernel(
           f32x4 acc[HT];
 #pragma unroll
           for (int t = 0; t < HT; ++t) acc[t] = f32x4{0.0f, 0.0f, 0.0f, 0.0f};
+          // Waves issuing MFMAs go first, so the matrix cores stay fed while
+          // other waves run their epilogues and stage copies (~4%).
+          __builtin_amdgcn_s_setprio(1);
 #pragma unroll
           for (int kk = 0; kk < KS; ++kk) {
             const bf16x8 kf = *reinterpret_cast<const bf16x8*>(kb + tt * kTileKeys * KST + kk * 32);
@@ -365,6 +368,7 @@ __global__ __launch_bounds__(kBlkThreads, 4) void indexer_block_kernel(
             for (int t = 0; t < HT; ++t)
               acc[t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qf[t][kk], kf, acc[t], 0, 0, 0);
           }
+          __builtin_amdgcn_s_setprio(0);
           float part = 0.0f;
 #pragma unroll
           for (int t = 0; t < HT; ++t) {
