@@ -126,7 +126,10 @@ int dsa_score_width(int rows, const int32_t* row_len, int* width);
  *   row_req      device [rows]                          int32
  *   row_len      device [rows]                          int32
  *   blocks       device [num_blocks][2] (first_row, n_rows) int32, or NULL
- *                for one row per block; rows of a block share a request
+ *                for one row per block; rows of a block are consecutive and
+ *                share a request (dsa_plan_blocks' plan): a block of several
+ *                rows is scored against its first row's block-table row, with
+ *                each key tile read once for all of its rows
  *   scores       device [rows][width]                   float32 (output)
  *
  * Supported: bf16 with head_dim in {64, 128}, num_heads in {32, 64} and
