@@ -380,6 +380,22 @@ def test_score_blocks_are_bit_identical():
         assert torch.equal(s.view(torch.int32), ref.view(torch.int32)), f"block_rows {br}"
 
 
+def test_score_blocks_fp32_bit_identical():
+    """fp32 inputs with prefill rows in score blocks (the fp32 kernel scores a
+    block's rows one after another): the same bits as one row per block, and
+    every row against the oracle."""
+    wl = I.custom(I.tiny(), name="tiny_prefill_fp32", prior=(30, 90, 0), new=(7, 10, 5), seed=17)
+    inp = _host_inputs(wl)
+    ref = run_step(inp, block_rows=1)
+    for br in (2, 4, 16):
+        st = run_step(inp, block_rows=br)
+        assert len(st.blocks_host) < st.rows
+        assert torch.equal(st.scores.view(torch.int32), ref.scores.view(torch.int32)), f"block_rows {br}"
+        assert torch.equal(st.idx, ref.idx)
+    e = _check_all(ref)
+    _say(f"fp32 score blocks, {ref.rows} rows: max errors {e}")
+
+
 def _block_mix(hi, di, page, seed=31):
     # Blocks of 37 (8+8+8+8+5 rows), 16, 9 (8+1) and 64 rows, and of 2, 3, 6,
     # 7 rows (4, 2, 1, 1 waves per row) for the block kernel, and one block
