@@ -2,10 +2,14 @@
 
 Scores and indices must match bit for bit; attention partials and outputs
 within max-abs 2e-2 (bf16 inputs) or 1e-5 (fp32 inputs), the log-sum-exp
-within 1e-3 / 1e-5. Small workloads are checked on every row; the three large
-workloads run at full size in the launch configuration the benchmark times,
-with sampled rows checked against the oracle and every row checked for the
-properties of a correct selection.
+within 1e-3 / 1e-5. Small workloads are checked on every row; the large ones
+(headline, ragged, mixed, 64 x 200K decode, 2048-row prefill at 1M context)
+run at full size in the launch configuration the benchmark times, with
+sampled rows checked against the oracle and every row checked for the
+properties of a correct selection. Alternative paths of the library (score
+blocks and the block indexer, two-stage top-k, row windows, the fused merge,
+graph replay, the scheduling hints) are checked bit for bit against the
+default ones.
 """
 
 import sys
