@@ -23,8 +23,8 @@
 //     the top, picks the digit holding the k-th largest;
 //   * it stops when the bits run out or every key still tied is needed.
 // The emit pass is an ordered compaction: each thread counts its keys above
-// the threshold prefix and equal to it, one block-wide exclusive scan gives
-// every thread its output offset, and keys equal to the prefix are taken in
+// the threshold prefix and equal to it, one block-wide exclusive scan of both
+// counts (each a full 32-bit sum) gives every thread its output offsets, and keys equal to the prefix are taken in
 // position order until the remaining need is met -- which is exactly
 // "ties to the lower position". Rows longer than a chunk re-read their
 // chunks from cache on every pass. Wave reductions and scans use DPP row
@@ -114,6 +114,37 @@ __device__ __forceinline__ uint32_t block_exclusive_scan(uint32_t v, uint32_t* s
   return base + incl - v;
 }
 
+// Exclusive prefix sums of two counts over the block in thread order, each
+// at full 32-bit width (a chunk can hold 65536 keys that all tie, so the two
+// counts cannot share one word); *ta / *tb get the totals. `sh` holds two
+// words per wave, used as in block_exclusive_scan.
+template <int kTopkWaves>
+__device__ __forceinline__ void block_exclusive_scan2(uint32_t a, uint32_t b, uint32_t* sh,
+                                                      uint32_t* ea, uint32_t* eb, uint32_t* ta,
+                                                      uint32_t* tb) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const uint32_t ia = wave_inclusive_scan(a);
+  const uint32_t ib = wave_inclusive_scan(b);
+  if (lane == 63) {
+    sh[wave] = ia;
+    sh[kTopkWaves + wave] = ib;
+  }
+  __syncthreads();
+  uint32_t ba = 0, bb = 0, sa = 0, sb = 0;
+#pragma unroll
+  for (int i = 0; i < kTopkWaves; ++i) {
+    const uint32_t x = sh[i], y = sh[kTopkWaves + i];
+    ba += (i < wave) ? x : 0u;
+    bb += (i < wave) ? y : 0u;
+    sa += x;
+    sb += y;
+  }
+  *ea = ba + ia - a;
+  *eb = bb + ib - b;
+  *ta = sa;
+  *tb = sb;
+}
+
 // What one workgroup selects from.
 enum TopkMode {
   kWholeRow = 0,  // row blockIdx.x, positions [0, row_len)
@@ -139,7 +170,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
   typedef typename std::conditional<(kVPT <= 32), uint32_t, uint64_t>::type Mask;
   static_assert(kVPT <= 64, "a thread's positions must fit one 64-bit mask");
   __shared__ uint32_t hist[2][kBins];  // alternate passes: one fills while the other is cleared
-  __shared__ uint32_t scan_sh[4][kTopkWaves];  // per-wave words of the block scans, by use
+  __shared__ uint32_t scan_sh[2][kTopkWaves];      // per-wave words of the radix passes' scans
+  __shared__ uint32_t emit_sh[2][2 * kTopkWaves];  // ... and of the emit's, by chunk parity
   __shared__ uint32_t red[2 * kTopkWaves];
   __shared__ uint32_t pick[3];
 
@@ -360,13 +392,13 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     const Mask vmask = nv == kVPT ? ~(Mask)0 : (((Mask)1 << nv) - 1);
     gtm &= vmask;
     eqm &= vmask;
-    uint32_t total;
+    uint32_t excl_gt, excl_eq, tot_gt, tot_eq;
     // Scans of consecutive chunks use different words; each scan's barrier
     // orders the reads of the one before.
-    const uint32_t excl = block_exclusive_scan<kTopkWaves>(
-        ((uint32_t)popcount(gtm) << 16) | (uint32_t)popcount(eqm), scan_sh[2 + (c & 1)], &total);
-    uint32_t g = gt_run + (excl >> 16);
-    uint32_t e = eq_run + (excl & 0xFFFFu);
+    block_exclusive_scan2<kTopkWaves>((uint32_t)popcount(gtm), (uint32_t)popcount(eqm),
+                                      emit_sh[c & 1], &excl_gt, &excl_eq, &tot_gt, &tot_eq);
+    uint32_t g = gt_run + excl_gt;
+    uint32_t e = eq_run + excl_eq;
     // The winners' keys (segment mode) are re-read from the row, a cache
     // hit: indexing key[] by the bit found at run time would move the whole
     // array out of registers.
@@ -391,8 +423,8 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
         ++e;
       }
     }
-    gt_run += total >> 16;
-    eq_run += total & 0xFFFFu;
+    gt_run += tot_gt;
+    eq_run += tot_eq;
   }
 }
 
