@@ -30,8 +30,9 @@
 //     only when a score overtakes it by more than 2^8; the running sum stays
 //     per lane and is reduced once at the end. Probabilities go to LDS.
 //   * values: fp32 FMAs of the fp32 probabilities into per-lane accumulators.
-// Padding slots (-1) sit at the end of a row's selection; a tile with no valid
-// slot ends the walk, and an empty split writes o = 0, lse = -inf.
+// Padding slots (-1) may sit anywhere in a split (dsa_topk puts them at the
+// end of a row): each has probability 0, the walk ends after the split's last
+// valid slot, and an empty split writes o = 0, lse = -inf.
 
 #include "dsa_kernels.h"
 
@@ -312,7 +313,9 @@ __global__ __launch_bounds__(64 * (FS > 0 ? FS * PP : 1), (sizeof(T) == 2 && D *
       }
 #pragma unroll
       for (int h = 0; h < G; ++h) {
-        const float p = fast_exp2(sc[h] - m[h]);  // -inf (padding) -> 0
+        // A padding slot has probability 0 whatever the reference: before the
+        // split's first valid slot m is still -inf, and -inf - -inf is NaN.
+        const float p = valid ? fast_exp2(sc[h] - m[h]) : 0.0f;
         lsum[h] += (hf == 0) ? p : 0.0f;
         if (hf == 0) p_lds[tl * G + h] = p;
       }

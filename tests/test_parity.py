@@ -188,6 +188,14 @@ def _topk_case_rows(width, k):
     # rows at the ranking limits: every key a candidate, with repeated values
     rows.append(("short ranked", (rng.integers(0, 40, 511) / 4).astype(np.float32)))
     rows.append(("short ranked mixed signs", rng.standard_normal(300).astype(np.float32)))
+    # a whole 65536-key chunk tied with the threshold (the emit's counts must
+    # not share one word): all equal, all zero (rectified scores), and 65536
+    # zeros ahead of a few positive scores
+    rows.append(("70000 equal", np.full(70000, 7.5, np.float32)))
+    rows.append(("70000 zeros", np.zeros(70000, np.float32)))
+    rows.append(("65536 zeros then positives",
+                 np.concatenate([np.zeros(65536, np.float32),
+                                 (rng.random(100) + 1).astype(np.float32)])))
     return rows
 
 
@@ -270,7 +278,7 @@ def _edge_batch(k):
 
 
 @pytest.mark.parametrize("k,chunk", [(1, 4), (16, 16), (16, 100), (16, 4096), (2048, 2048),
-                                     (2048, 8192), (2048, 40000)])
+                                     (2048, 8192), (2048, 40000), (16, 70000), (2048, 70000)])
 def test_topk_chunked_edges(k, chunk):
     """The two-stage selection (segment winners, then the row's top-k among
     them) against the oracle, and bit for bit against the one-pass kernel."""
@@ -350,6 +358,82 @@ def test_windowed_fp32_tiny():
     assert torch.equal(idx, step.idx)
     for r in range(step.rows):
         check_row(step, r)
+
+
+def _gapped_idx(step, rng):
+    """Caller-given selections with -1 anywhere (allowed by the contract):
+    a leading run of more than one 32-slot tile, a fully empty quarter, gaps
+    in the middle; valid slots hold distinct positions below the row length."""
+    k = step.wl.topk
+    out = np.full((step.rows, k), -1, np.int32)
+    for r in range(step.rows):
+        L = int(step.row_len_host[r])
+        n = min(L, k)
+        pos = rng.permutation(L)[:n].astype(np.int32)
+        slots = np.arange(k)
+        keep = (slots >= 40) & ~((slots >= k // 4) & (slots < k // 2))
+        keep &= ~((slots >= 3 * k // 4 + 7) & (slots < 3 * k // 4 + 45))
+        keep_slots = slots[keep][:n]
+        out[r, keep_slots] = pos[: len(keep_slots)]
+    return out
+
+
+def _oracle_attention(step, r, idx_row, S):
+    inp, wl = step.inp, step.wl
+    req = int(step.row_req_host[r])
+    bt = inp.block_table[req]
+    valid = idx_row >= 0
+    n = int(valid.sum())
+    kc = np.zeros((max(n, 1), 1, wl.hkv, wl.d))
+    vc = np.zeros((max(n, 1), 1, wl.hkv, wl.d))
+    if n:
+        p = torch.from_numpy(idx_row[valid].astype(np.int64)).to(inp.q.device)
+        pages = bt[p // wl.page].long()
+        kc[:n, 0] = inp.k_cache[pages, p % wl.page].double().cpu().numpy()
+        vc[:n, 0] = inp.v_cache[pages, p % wl.page].double().cpu().numpy()
+    local = np.full(len(idx_row), -1, np.int64)
+    local[valid] = np.arange(n)
+    q = inp.q[r].double().cpu().numpy()
+    po, pl = O.attention_split_row(q, kc, vc, np.arange(max(n, 1)), 1, local, wl.attn_scale, S)
+    return po, pl, *O.merge_row(po, pl)
+
+
+@pytest.mark.parametrize("S", [1, 2, 4, 8])
+def test_attention_padding_anywhere(S):
+    """Selections with -1 runs at the start of a split, in its middle, and
+    whole empty splits: padding slots weigh nothing, nothing turns NaN, and
+    partials (two launches) and outputs (fused) match the oracle."""
+    from sparse_attention_decode_02_amd import lib
+    _say(f"attention with padding anywhere, splits {S}")
+    step = run_step(_host_inputs(_small_mixed(seed=41)), num_splits=S)
+    wl, inp = step.wl, step.inp
+    gidx = _gapped_idx(step, np.random.default_rng(S))
+    idx_d = torch.from_numpy(gidx).cuda()
+    po = torch.empty_like(step.part_o)
+    pl = torch.empty_like(step.part_lse)
+    lib.sparse_attn(inp.q, inp.k_cache, inp.v_cache, inp.block_table, step.row_req, idx_d,
+                    wl.page, wl.attn_scale, S, po, pl)
+    out = torch.empty_like(step.out)
+    out_lse = torch.empty_like(step.out_lse)
+    lib.sparse_attn_merged(inp.q, inp.k_cache, inp.v_cache, inp.block_table, step.row_req, idx_d,
+                           wl.page, wl.attn_scale, S, out, out_lse)
+    torch.cuda.synchronize()
+    assert not bool(torch.isnan(po).any()) and not bool(torch.isnan(out.float()).any())
+    tol_o, tol_l = 2e-2, 1e-3
+    for r in range(step.rows):
+        wpo, wpl, wo, wl_ = _oracle_attention(step, r, gidx[r], S)
+        gpl = pl[r].double().cpu().numpy()
+        assert np.array_equal(np.isfinite(gpl), np.isfinite(wpl)), r
+        fin = np.isfinite(wpl)
+        if fin.any():
+            assert float(np.abs(gpl[fin] - wpl[fin]).max()) <= tol_l, r
+        assert float(np.abs(po[r].double().cpu().numpy() - wpo).max()) <= tol_o, r
+        assert float(np.abs(out[r].double().cpu().numpy() - wo).max()) <= tol_o, r
+        gl = out_lse[r].double().cpu().numpy()
+        assert np.array_equal(np.isfinite(gl), np.isfinite(wl_)), r
+        fl = np.isfinite(wl_)
+        if fl.any():
+            assert float(np.abs(gl[fl] - wl_[fl]).max()) <= tol_l, r
 
 
 def test_padding_rows_with_zero_length():
