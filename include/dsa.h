@@ -32,7 +32,10 @@
  *   "Treat every query token of a step ... as a row": launch sizes depend only
  *   on the padded batch; the PR description: graph replay with changing token
  *   positions and active lengths).
- * - The calls are thread-safe: the library keeps no mutable global state.
+ * - The calls are thread-safe: the library keeps no mutable global state,
+ *   except the fixed per-device workspace of dsa_topk_chunked_noalloc (and
+ *   its device address, looked up once per device), whose calls must not
+ *   overlap on one device.
  */
 #ifndef DSA_H
 #define DSA_H
@@ -215,6 +218,32 @@ int dsa_topk_chunked(const float* scores, const int32_t* row_len, int rows, int 
 
 /* Candidate slots dsa_topk_chunked needs for these sizes (host). */
 int dsa_topk_chunked_slots(int rows, int width, int k, int chunk, long long* slots);
+
+/* ------------------------------------------------------------------------
+ * dsa_topk_chunked_noalloc -- dsa_topk_chunked without a caller workspace,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).
+ *
+ * Same selection and result as dsa_topk_chunked, bit for bit. The candidate
+ * workspace is a fixed array inside the library, DSA_TOPK_NOALLOC_MAX_SLOTS
+ * int32 slots (16 MiB) on each device the library runs on, held until the
+ * process ends; the call allocates and frees nothing. Every call on a device
+ * shares that device's array and leaves its contents behind (nothing in it
+ * needs clearing: stage 1 writes every entry stage 2 reads). Calls that
+ * overlap on one device -- on two streams, or from two host threads without
+ * ordering -- race on the array and give undefined results.
+ *
+ *   scores, row_len, idx, k, chunk: as for dsa_topk_chunked
+ *
+ * Sizes needing more than DSA_TOPK_NOALLOC_MAX_SLOTS candidate slots
+ * (dsa_topk_chunked_slots; e.g. 64 rows of 204800 positions with k = 2048 and
+ * chunk = 32768 need 1835008) return DSA_ERR_WORKSPACE before any launch;
+ * other errors as for dsa_topk_chunked; DSA_ERR_LAUNCH also when the array's
+ * device address cannot be found on the current device.
+ * ------------------------------------------------------------------------ */
+#define DSA_TOPK_NOALLOC_MAX_SLOTS (1LL << 22)
+int dsa_topk_chunked_noalloc(const float* scores, const int32_t* row_len, int rows, int width,
+                             int k, int chunk, int32_t* idx, void* stream);
 
 /* The segment length at which dsa_topk_chunked is expected to beat dsa_topk
  * on the current device for these sizes, or 0 (host): rows longer than one

@@ -6,6 +6,7 @@
 #include <math.h>
 
 #include <algorithm>
+#include <atomic>
 
 #include "../../include/dsa.h"
 #include "dsa_kernels.h"
@@ -109,7 +110,54 @@ int topk_chunked_check(int rows, int width, int k, int chunk, long long* slots) 
 
 }  // namespace
 
+// ---- The allocation-free two-stage top-k's workspace -----------------------
+// dsa_topk_chunked_noalloc keeps the segment winners (positions, then keys)
+// in this array instead of a caller-given buffer. Each device that loads the
+// library holds its own copy until the process ends. In host code the name
+// `scratch` stands for a host-side shadow, not device memory: only the device
+// address looked up below (scratch_on_device) is ever passed to a kernel.
+static __device__ __align__(256) int32_t scratch[DSA_TOPK_NOALLOC_MAX_SLOTS];
+
+namespace {
+
+constexpr int kMaxScratchDevices = 1024;
+std::atomic<int32_t*> g_scratch_ptr[kMaxScratchDevices];
+
+// Device address of `scratch` on device `dev` (the current device), looked up
+// with hipGetSymbolAddress on the first call there and kept; NULL on failure.
+int32_t* scratch_on_device(int dev) {
+  int32_t* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* addr = nullptr;
+  if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || addr == nullptr)
+    return nullptr;
+  p = static_cast<int32_t*>(addr);
+  g_scratch_ptr[dev].store(p, std::memory_order_release);  // the same address if two threads race
+  return p;
+}
+
+}  // namespace
+
 extern "C" {
+
+int dsa_topk_chunked_noalloc(const float* scores, const int32_t* row_len, int rows, int width,
+                             int k, int chunk, int32_t* idx, void* stream) {
+  int st = topk_check(scores, row_len, rows, width, k, idx);
+  if (st != DSA_OK) return st;
+  long long need = 0;
+  st = topk_chunked_check(rows, width, k, chunk, &need);
+  if (st != DSA_OK) return st;
+  if (need > DSA_TOPK_NOALLOC_MAX_SLOTS) return DSA_ERR_WORKSPACE;
+  if (rows == 0) return DSA_OK;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxScratchDevices)
+    return DSA_ERR_LAUNCH;
+  int32_t* cand = scratch_on_device(dev);
+  if (!cand) return DSA_ERR_LAUNCH;
+  // Stage 1 writes every candidate stage 2 reads, so nothing is cleared.
+  return launch_status(dsa::launch_topk_chunked(scores, row_len, rows, width, k, chunk, cand, idx,
+                                                static_cast<hipStream_t>(stream)));
+}
 
 int dsa_indexer_scores_total(const void* q_idx, const float* w, const void* k_idx_cache,
                              const int32_t* block_table, const int32_t* row_req,

@@ -44,6 +44,7 @@ _SIGS = {
     "dsa_topk": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "dsa_topk_total": (_I, [_P, _P, _I, _I, _I, _LL, _P, _P]),
     "dsa_topk_chunked": (_I, [_P, _P, _I, _I, _I, _I, _P, _LL, _P, _P]),
+    "dsa_topk_chunked_noalloc": (_I, [_P, _P, _I, _I, _I, _I, _P, _P]),
     "dsa_topk_chunked_slots": (_I, [_I, _I, _I, _I, ctypes.POINTER(_LL)]),
     "dsa_topk_chunk_suggest": (_I, [_I, _I, _I, _LL, ctypes.POINTER(_I)]),
     "dsa_indexer_topk_windowed": (_I, [_P, _P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I,
@@ -237,6 +238,19 @@ def topk_chunked(scores, row_len, k, chunk, cand, idx, stream=None, prepare=Fals
         _dev(scores, "scores", torch.float32), _dev(row_len, "row_len", torch.int32), rows, width,
         int(k), int(chunk), _dev(cand, "cand", torch.int32), int(cand.numel()),
         _dev(idx, "idx", torch.int32)], stream, prepare)
+    return p if prepare else idx
+
+
+TOPK_NOALLOC_MAX_SLOTS = 1 << 22  # DSA_TOPK_NOALLOC_MAX_SLOTS
+
+
+def topk_chunked_noalloc(scores, row_len, k, chunk, idx, stream=None, prepare=False):
+    """dsa_topk_chunked_noalloc: dsa_topk_chunked with the library's own fixed
+    candidate workspace (no allocation; calls on one device must not overlap)."""
+    rows, width = scores.shape
+    p = _call("dsa_topk_chunked_noalloc", [
+        _dev(scores, "scores", torch.float32), _dev(row_len, "row_len", torch.int32), rows, width,
+        int(k), int(chunk), _dev(idx, "idx", torch.int32)], stream, prepare)
     return p if prepare else idx
 
 

@@ -197,6 +197,32 @@ def test_topk_chunked_rejects(kw, code):
     assert lib._lib.dsa_topk_chunked(*_chunked_args(**kw)) == code
 
 
+def _noalloc_args(**kw):
+    a = dict(scores=A, row_len=A, rows=4, width=128, k=16, chunk=32, idx=A, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(scores=None), NULL), (dict(row_len=None), NULL), (dict(idx=None), NULL),
+    (dict(chunk=8), SHAPE), (dict(chunk=30), SHAPE), (dict(k=0), SHAPE), (dict(width=66), SHAPE),
+    (dict(scores=A + 4), ALIGN), (dict(rows=0), OK),
+    # 2 * rows * segments * k > DSA_TOPK_NOALLOC_MAX_SLOTS (1 << 22)
+    (dict(rows=2048, width=4096, k=2048, chunk=2048), WS),
+    (dict(rows=1025, width=4096, k=2048, chunk=4096), WS),
+])
+def test_topk_chunked_noalloc_rejects(kw, code):
+    """Every status of the allocation-free call but a launch is decided on the
+    host: oversized inputs are refused before the workspace is looked up."""
+    assert lib._lib.dsa_topk_chunked_noalloc(*_noalloc_args(**kw)) == code
+
+
+def test_topk_chunked_noalloc_limit():
+    assert lib.TOPK_NOALLOC_MAX_SLOTS == 1 << 22
+    assert lib.topk_chunked_slots(1024, 4096, 2048, 4096) == 1 << 22  # exactly fits
+    assert lib.topk_chunked_slots(64, 204800, 2048, 32768) <= lib.TOPK_NOALLOC_MAX_SLOTS
+
+
 def test_topk_chunked_slots():
     assert lib.topk_chunked_slots(4, 128, 16, 32) == 2 * 4 * 4 * 16
     assert lib.topk_chunked_slots(4, 132, 16, 32) == 2 * 4 * 5 * 16
