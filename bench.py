@@ -17,7 +17,10 @@ Prints one JSON line:
                  average duration (HIP events on the launch stream), against
                  8 TB/s
   cpu_baseline   the CPU oracle timed on a bounded sample of rows of the same
-                 workload, extrapolated to the whole layer
+                 workload (paged gathers included), extrapolated to the whole
+                 layer, on every core this process may use and on one core
+  configs        latency, GB/s and fraction of 8 TB/s of the other workloads
+                 (tiny, decode, ragged, mixed), measured in the same run
 """
 
 from __future__ import annotations
@@ -154,85 +157,179 @@ def time_kernels(step, steps, torch):
     return {n: 1000.0 * sum(a.elapsed_time(b) for a, b in evs[n]) / steps for n, _ in stages}
 
 
-def cpu_baseline(step, budget_s, torch):
-    """The oracle, as it stands, on a bounded sample of rows of this workload."""
-    import numpy as np
+class _Bf16Host:
+    """A bf16 tensor held on the host as its raw 16-bit words. Indexing it
+    returns the float64 values (exact), so the oracle's own paged gathers
+    read the caches through the block table as they would a float array."""
 
-    from oracle import dsa_oracle as O
+    def __init__(self, words):
+        self.words = words
+        self.shape = words.shape
+
+    def __getitem__(self, key):
+        import numpy as np
+        u = np.asarray(self.words[key]).astype(np.uint32) << 16
+        return u.view(np.float32).astype(np.float64)
+
+
+def _host_tensor(t, torch):
+    """Host copy of a device tensor for the oracle: bf16 as _Bf16Host, other
+    dtypes as NumPy arrays."""
+    if t.dtype == torch.bfloat16:
+        return _Bf16Host(t.view(torch.int16).cpu().numpy().view("uint16"))
+    return t.cpu().numpy()
+
+
+def _cpu_model():
     try:
-        from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
-    except Exception:  # pragma: no cover
-        threads = 1
-    inp, wl = step.inp, step.wl
-    dev = inp.q.device
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
-    def host(t):
-        return t.detach().to("cpu", torch.float64).numpy()
 
-    rng = np.random.default_rng(0)
-    order = rng.permutation(step.rows)
-    # Rows in a seeded order, over as many passes as the budget allows (a
-    # small layer is timed several times over). A row's host copies are
-    # gathered once and kept (up to a few GB), so repeats cost only the
-    # timed oracle work.
-    order = np.tile(order, max(1, int(np.ceil(1e6 / max(1, step.rows)))))
-    cache, cached_bytes, cache_cap = {}, 0, 6 << 30
-    spent, rows_done, row_lens = 0.0, [], []
-    for r in order.tolist():
+def _oracle_pass(step, host, rows_order, budget_s):
+    """Runs the oracle over rows in the given order until the budget is
+    spent. Timed per row: the paged gathers of the indexer keys and of the
+    selected K/V (through the block table), the indexer, the top-k, the split
+    attention and the merge. Returns (seconds, rows done, their lengths)."""
+    from oracle import dsa_oracle as O
+    wl = step.wl
+    kI_c, k_c, v_c, bt, qI, w, q = host
+    spent, done, lens = 0.0, [], []
+    for r in rows_order:
         L = int(step.row_len_host[r])
         req = int(step.row_req_host[r])
-        bt = inp.block_table[req]
-        hit = cache.get(r)
-        if hit is None:
-            pos = torch.arange(L, device=dev)
-            kI = host(inp.kI_cache[bt[pos // wl.page].long(), pos % wl.page])
-            qI, w, q = host(inp.qI[r]), host(inp.w[r]), host(inp.q[r])
-        else:
-            qI, w, q, kI, kc, vc, local = hit
         t0 = time.perf_counter()
-        s = O.indexer_scores_row(qI, w, kI)
-        idx = O.topk_row(s, L, wl.topk)
-        t1 = time.perf_counter()
-        if hit is None:
-            sel = idx[idx >= 0]
-            n = len(sel)
-            kc = np.zeros((wl.topk, 1, wl.hkv, wl.d))
-            vc = np.zeros((wl.topk, 1, wl.hkv, wl.d))
-            p = torch.from_numpy(sel.astype(np.int64)).to(dev)
-            pages = bt[p // wl.page].long()
-            kc[:n, 0] = host(inp.k_cache[pages, p % wl.page])
-            vc[:n, 0] = host(inp.v_cache[pages, p % wl.page])
-            local = np.full(wl.topk, -1, np.int64)
-            local[:n] = np.arange(n)
-            nbytes = sum(a.nbytes for a in (qI, w, q, kI, kc, vc, local))
-            if cached_bytes + nbytes <= cache_cap:
-                cache[r] = (qI, w, q, kI, kc, vc, local)
-                cached_bytes += nbytes
-        t2 = time.perf_counter()
-        po, pl = O.attention_split_row(q, kc, vc, np.arange(wl.topk), 1, local, wl.attn_scale,
+        kI = O.gather_logical(kI_c, bt[req], L, wl.page)
+        sc = O.indexer_scores_row(qI[r], w[r], kI)
+        idx = O.topk_row(sc, L, wl.topk)
+        po, pl = O.attention_split_row(q[r], k_c, v_c, bt[req], wl.page, idx, wl.attn_scale,
                                        step.num_splits)
         O.merge_row(po, pl)
-        t3 = time.perf_counter()
-        spent += (t1 - t0) + (t3 - t2)
-        rows_done.append(r)
-        row_lens.append(L)
+        spent += time.perf_counter() - t0
+        done.append(r)
+        lens.append(L)
         if spent >= budget_s:
             break
-    # scale by row length share so ragged samples extrapolate fairly
-    total_len = float(sum(int(x) for x in step.row_len_host))
-    share = sum(row_lens) / total_len if total_len else 1.0
-    est_s = spent / share if share > 0 else spent
+    return spent, done, lens
+
+
+def cpu_baseline(step, budget_s, torch):
+    """The oracle, as it stands, on a bounded sample of rows of this workload:
+    once with the BLAS on every host core this process may use (capped by
+    OMP_NUM_THREADS when set) and once on one core. Each run takes about
+    ``budget_s`` seconds and is scaled to the whole layer by the sampled rows'
+    share of its keys."""
+    import numpy as np
+    from threadpoolctl import threadpool_limits
+
+    inp = step.inp
+    affinity = len(os.sched_getaffinity(0))
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    threads = min(affinity, int(env)) if env.isdigit() and int(env) > 0 else affinity
+    f64 = lambda t: t.detach().to("cpu", torch.float64).numpy()
+    host = (_host_tensor(inp.kI_cache, torch), _host_tensor(inp.k_cache, torch),
+            _host_tensor(inp.v_cache, torch), inp.block_table.cpu().numpy(),
+            f64(inp.qI), f64(inp.w), f64(inp.q))
+    rng = np.random.default_rng(0)
+    order = np.concatenate([rng.permutation(step.rows) for _ in range(64)]).tolist()
+    total_len = float(sum(int(x) for x in step.row_len_host)) or 1.0
+    out = {}
+    for n in (threads, 1):
+        with threadpool_limits(limits=n):
+            spent, done, lens = _oracle_pass(step, host, order, budget_s)
+        share = sum(lens) / total_len
+        out[n] = (spent / share if share > 0 else spent, spent, len(done), len(set(done)), share)
+    est, spent, n_done, n_distinct, share = out[threads]
+    est1, spent1, n1, _, share1 = out[1]
     return {
-        "value": round(est_s * 1e6, 1),
+        "value": round(est * 1e6, 1),
         "unit": "us",
         "cores": int(threads),
         "kind": "oracle",
-        "sample": (f"{len(rows_done)} row evaluations ({len(set(rows_done))} distinct of "
-                   f"{step.rows} rows; full indexer + top-k + attention + merge each, float64 "
-                   f"NumPy), {spent:.1f} s, scaled by their share of the layer's keys "
-                   f"({share:.4f}); gathers and host copies not timed"),
+        "sample": (f"{n_done} row evaluations ({n_distinct} distinct of {step.rows} rows), "
+                   f"{spent:.1f} s on {threads} threads, scaled to the layer by their share of "
+                   f"its keys ({share:.3f}); timed per row: paged gathers through the block "
+                   f"table, indexer, top-k, split attention, merge (float64 NumPy)"),
+        "one_core": {"value": round(est1 * 1e6, 1), "unit": "us",
+                     "sample": f"{n1} row evaluations, {spent1:.1f} s, share {share1:.3f}"},
+        "cpu_model": _cpu_model(),
+        "host_cores_available": affinity,
     }
+
+
+def measure_configs(names, steps, warmup, torch):
+    """Latency, algorithmic GB/s and fraction of 8 TB/s for other workloads,
+    each generated on the device and timed like the headline (the bench's
+    default step configuration), then freed."""
+    from sparse_attention_decode_02_amd import inputs as I
+    from sparse_attention_decode_02_amd.step import DsaStep
+    out = {}
+    for name in names:
+        wl = I.WORKLOADS[name]()
+        print(f"[bench] config {wl.name}", file=sys.stderr, flush=True)
+        inp = I.generate(wl, "cuda")
+        step = DsaStep(inp, block_rows=8, fused=None, topk_chunk=None)
+        torch.cuda.synchronize()
+        ms = time_steps(step, steps, warmup, torch)
+        kern = time_kernels(step, max(5, steps // 4), torch)
+        ab = algorithmic_bytes(wl, step.row_len_host)
+        total = sum(ab.values())
+        us = ms * 1000.0
+        gbps = total / (us * 1e-6) / 1e9
+        rec = {"workload": wl.name, "rows": step.rows, "latency_us": round(us, 2),
+               "algorithmic_bytes": total, "gbps": round(gbps, 1),
+               "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
+               "kernels_us": {n: round(v, 2) for n, v in kern.items()},
+               "attention_splits": step.num_splits}
+        if len(set(step.row_req_host.tolist())) < step.rows:
+            # Rows of one request share its keys: the bytes HBM must deliver
+            # at least (each request's indexer keys and distinct selected K/V
+            # once) are far fewer than the per-row bytes the method issues,
+            # most of which the caches serve. GB/s and the fraction of the
+            # peak are taken on the compulsory bytes.
+            comp = compulsory_bytes(step, wl, torch)
+            cg = comp / (us * 1e-6) / 1e9
+            rec.update({"algorithmic_bytes": comp, "gbps": round(cg, 1),
+                        "frac_of_hbm_peak": round(cg / HBM_PEAK_GBPS, 4),
+                        "method_issued_bytes": total, "method_issued_gbps": round(gbps, 1),
+                        "bytes_note": ("algorithmic_bytes: each request's indexer keys and "
+                                       "distinct selected K/V rows once, every row's scores, "
+                                       "queries, indices and outputs; method_issued_bytes: "
+                                       "every row's own key reads and gathers")})
+        out[name] = rec
+        del step, inp
+        torch.cuda.empty_cache()
+    return out
+
+
+def compulsory_bytes(step, wl, torch):
+    """Bytes a step must move at least when rows share a request: each
+    request's indexer keys once (its longest row), every row's score write
+    and read, qI, w, q, out and indices, and each request's distinct selected
+    K/V rows once."""
+    e = 2 if wl.dtype == "bf16" else 4
+    req = step.row_req_host
+    lens = step.row_len_host
+    b = 0
+    longest = {}
+    for q, L in zip(req.tolist(), lens.tolist()):
+        longest[q] = max(longest.get(q, 0), L)
+    for L in longest.values():
+        b += L * wl.di * e + 4 * -(-L // wl.page)
+    b += int(sum(8 * int(L) for L in lens))  # scores written, read
+    b += step.rows * (wl.hi * wl.di * e + 4 * wl.hi + 2 * wl.hq * wl.d * e + 8 * wl.topk)
+    idx = step.idx
+    rq = step.row_req.long()
+    for q in longest:
+        sel = idx[rq == q]
+        n = int(torch.unique(sel[sel >= 0]).numel())
+        b += n * wl.hkv * wl.d * e * 2
+    return int(b)
 
 
 def main(argv=None):
@@ -256,8 +353,10 @@ def main(argv=None):
                          "(0 = every row at once)")
     ap.add_argument("--graph", action="store_true",
                     help="record the step into a HIP graph once and time its replays")
-    ap.add_argument("--cpu-seconds", type=float, default=12.0,
-                    help="oracle time budget for cpu_baseline (0 = skip)")
+    ap.add_argument("--cpu-seconds", type=float, default=8.0,
+                    help="oracle time budget for cpu_baseline, per core setting (0 = skip)")
+    ap.add_argument("--configs", default="tiny,decode,ragged,mixed",
+                    help="other workloads measured in the same run (comma list, '' = none)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the step, run a plain device copy of this many MiB "
                          "(calibrates HBM byte counters)")
@@ -291,10 +390,11 @@ def main(argv=None):
     print(f"[bench] generating {wl.name} on the device", file=sys.stderr, flush=True)
     inp = I.generate(wl, "cuda")
     block_rows = args.block_rows
-    step = DsaStep(inp, num_splits=args.splits or None, block_rows=block_rows,
-                   fused=False if args.unfused else None,
-                   topk_chunk=None if args.topk_chunk < 0 else args.topk_chunk,
-                   score_buffer_bytes=(args.score_buffer_mib << 20) if args.score_buffer_mib else None)
+    opts = dict(num_splits=args.splits or None, block_rows=block_rows,
+                fused=False if args.unfused else None,
+                topk_chunk=None if args.topk_chunk < 0 else args.topk_chunk,
+                score_buffer_bytes=(args.score_buffer_mib << 20) if args.score_buffer_mib else None)
+    step = DsaStep(inp, **opts)
     torch.cuda.synchronize()
     print(f"[bench] rows {step.rows} width {step.width} splits {step.num_splits}",
           file=sys.stderr, flush=True)
@@ -376,7 +476,13 @@ def main(argv=None):
         },
     }
     if args.cpu_seconds > 0:
+        print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds, torch)
+    names = [n for n in args.configs.split(",") if n and n != args.workload]
+    if names:
+        del step, inp, graph
+        torch.cuda.empty_cache()
+        result["configs"] = measure_configs(names, args.steps, args.warmup, torch)
     print(json.dumps(result), flush=True)
     return 0
 

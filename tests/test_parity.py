@@ -4,9 +4,10 @@ Scores and indices must match bit for bit; attention partials and outputs
 within max-abs 2e-2 (bf16 inputs) or 1e-5 (fp32 inputs), the log-sum-exp
 within 1e-3 / 1e-5. Small workloads are checked on every row; the large ones
 (headline, ragged, mixed, 64 x 200K decode, 2048-row prefill at 1M context)
-run at full size in the launch configuration the benchmark times, with
-sampled rows checked against the oracle and every row checked for the
-properties of a correct selection. Alternative paths of the library (score
+run at full size in the launch configuration the benchmark times: every row
+of the headline and ragged batches, every decode row and every 64th prefill
+row of the mixed step against the oracle (sampled rows of the two largest),
+and every row checked for the properties of a correct selection. Alternative paths of the library (score
 blocks and the block indexer, two-stage top-k, row windows, the fused merge,
 graph replay, the scheduling hints) are checked bit for bit against the
 default ones.
@@ -649,17 +650,19 @@ def _full(wl, rows_fn):
     _same_selection_other_ways(step)
     rows = rows_fn(step)
     errs = {}
-    for r in rows:
+    for i, r in enumerate(rows):
         e = check_row(step, r)
         errs = {k: max(errs.get(k, 0.0), v) for k, v in e.items()}
-        _say(f"  row {r} (L={int(step.row_len_host[r])}) ok")
+        if i % 16 == 15 or i == len(rows) - 1:
+            _say(f"  {i + 1}/{len(rows)} rows ok (last: row {r}, L={int(step.row_len_host[r])})")
     _say(f"  max errors {errs}")
     del step, inp
     torch.cuda.empty_cache()
 
 
 def test_headline_full_size():
-    _full(I.headline(), lambda s: [0, 1, 37, s.rows - 1])
+    """Every row of the batch-64, 32K-context decode against the oracle."""
+    _full(I.headline(), lambda s: list(range(s.rows)))
 
 
 def test_prefill_1m_full_size():
@@ -673,15 +676,21 @@ def test_long_context_full_size():
 
 
 def test_ragged_full_size():
+    """Every row of the ragged batch (lengths 1 .. 65536) against the oracle."""
     def rows(s):
         L = s.row_len_host
-        short = [r for r in range(s.rows) if 1 < L[r] < 2048]
-        return sorted({int(np.argmin(L)), int(np.argmax(L)), short[0], 5, 50})
+        assert int(L.min()) == 1 and int(L.max()) == 65536
+        assert any(1 < x < 2048 for x in L)
+        return list(range(s.rows))
     _full(I.ragged(), rows)
 
 
 def test_mixed_full_size():
+    """All 60 decode rows, every 64th prefill row and the last row of each
+    prefill request against the oracle."""
     def rows(s):
-        L = s.row_len_host
-        return sorted({0, 511, 512, 2047, int(np.argmax(L)), 2050, s.rows - 1})
+        n_pre = int(sum(n for n in s.wl.new if n > 1))
+        assert n_pre == 2048 and s.rows == 2108
+        pre = set(range(0, n_pre, 64)) | {511, 512, 1023, 1535, 2047}
+        return sorted(pre | set(range(n_pre, s.rows)))
     _full(I.mixed(), rows)
