@@ -86,17 +86,28 @@ def _events(torch):
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
 
-def time_steps(step, steps, warmup, torch, graph=None):
+def time_steps(step, steps, warmup, torch, graph=None, trace=None):
+    """Mean step time (ms) of ``steps`` steps after ``warmup``, one event
+    before and one after. With a ``trace`` list, events between the steps
+    (recorded on the same stream, so they add no wait) give each step's time
+    in microseconds too."""
     run = graph.replay if graph is not None else step.run
     for _ in range(warmup):
         run()
     torch.cuda.synchronize()
+    evs = [_events(torch)[0] for _ in range(steps + 1)] if trace is not None else None
     a, b = _events(torch)
     a.record()
-    for _ in range(steps):
+    for i in range(steps):
+        if evs:
+            evs[i].record()
         run()
+    if evs:
+        evs[steps].record()
     b.record()
     torch.cuda.synchronize()
+    if evs:
+        trace.extend(round(1000.0 * evs[i].elapsed_time(evs[i + 1]), 1) for i in range(steps))
     return a.elapsed_time(b) / steps  # ms
 
 
@@ -122,7 +133,7 @@ def _pct(v, q):
     return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
 
 
-def read_floor_gbps(torch, mib=1024, reps=10):
+def read_floor_gbps(torch, mib=1024, reps=50):
     """A plain streaming read of ``mib`` MiB (dsa_read_probe): the practical
     read bandwidth the layer's GB/s is compared with."""
     from sparse_attention_decode_02_amd import lib
@@ -269,11 +280,14 @@ def measure_configs(names, steps, warmup, torch):
     from sparse_attention_decode_02_amd import inputs as I
     from sparse_attention_decode_02_amd.step import DsaStep
     out = {}
-    for name in names:
+    for spec in names:
+        name, _, opt = spec.partition("+")
+        hist = opt == "hist"
         wl = I.WORKLOADS[name]()
-        print(f"[bench] config {wl.name}", file=sys.stderr, flush=True)
+        print(f"[bench] config {wl.name}{' (histogram top-k)' if hist else ''}", file=sys.stderr,
+              flush=True)
         inp = I.generate(wl, "cuda")
-        step = DsaStep(inp, block_rows=8, fused=None, topk_chunk=None)
+        step = DsaStep(inp, block_rows=8, fused=None, topk_chunk=0 if hist else None, hist=hist)
         torch.cuda.synchronize()
         ms = time_steps(step, steps, warmup, torch)
         kern = time_kernels(step, max(5, steps // 4), torch)
@@ -285,7 +299,10 @@ def measure_configs(names, steps, warmup, torch):
                "algorithmic_bytes": total, "gbps": round(gbps, 1),
                "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
                "kernels_us": {n: round(v, 2) for n, v in kern.items()},
-               "attention_splits": step.num_splits}
+               "attention_splits": step.num_splits,
+               "topk_mode": ("from the indexer's score histogram" if step.use_hist else
+                             f"two-stage, {step.topk_chunk}-position segments"
+                             if step.topk_chunk else "one pass")}
         if len(set(step.row_req_host.tolist())) < step.rows:
             # Rows of one request share its keys: the bytes HBM must deliver
             # at least (each request's indexer keys and distinct selected K/V
@@ -301,7 +318,7 @@ def measure_configs(names, steps, warmup, torch):
                                        "distinct selected K/V rows once, every row's scores, "
                                        "queries, indices and outputs; method_issued_bytes: "
                                        "every row's own key reads and gathers")})
-        out[name] = rec
+        out[spec] = rec
         del step, inp
         torch.cuda.empty_cache()
     return out
@@ -351,12 +368,16 @@ def main(argv=None):
     ap.add_argument("--score-buffer-mib", type=int, default=0,
                     help="score and select in row windows through a buffer of this many MiB "
                          "(0 = every row at once)")
+    ap.add_argument("--hist", type=int, default=0,
+                    help="1: the indexer counts each row's scores and the top-k starts from the "
+                         "counts (dsa_indexer_scores_hist + dsa_topk_hist)")
     ap.add_argument("--graph", action="store_true",
                     help="record the step into a HIP graph once and time its replays")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="oracle time budget for cpu_baseline, per core setting (0 = skip)")
-    ap.add_argument("--configs", default="tiny,decode,ragged,mixed",
-                    help="other workloads measured in the same run (comma list, '' = none)")
+    ap.add_argument("--configs", default="tiny,decode,ragged,mixed,ragged+hist,long,long+hist",
+                    help="other workloads measured in the same run (comma list, '' = none; "
+                         "name+hist: with the histogram top-k)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the step, run a plain device copy of this many MiB "
                          "(calibrates HBM byte counters)")
@@ -393,20 +414,26 @@ def main(argv=None):
     opts = dict(num_splits=args.splits or None, block_rows=block_rows,
                 fused=False if args.unfused else None,
                 topk_chunk=None if args.topk_chunk < 0 else args.topk_chunk,
-                score_buffer_bytes=(args.score_buffer_mib << 20) if args.score_buffer_mib else None)
+                score_buffer_bytes=(args.score_buffer_mib << 20) if args.score_buffer_mib else None,
+                hist=bool(args.hist))
     step = DsaStep(inp, **opts)
     torch.cuda.synchronize()
     print(f"[bench] rows {step.rows} width {step.width} splits {step.num_splits}",
           file=sys.stderr, flush=True)
 
     graph = step.capture() if args.graph else None
-    ms = time_steps(step, args.steps, args.warmup, torch, graph)
+    # The read floor is measured first, over ~8 ms of streaming reads: this
+    # also brings the GPU to its working clocks, which it otherwise reaches
+    # only ~10 ms into a run (steps timed right after a short warm-up measure
+    # ~5% slower than the same steps later in the run).
+    floor = read_floor_gbps(torch)
+    trace = []
+    ms = time_steps(step, args.steps, args.warmup, torch, graph, trace)
     kern = time_kernels(step, args.steps, torch)
     warm = time_per_step(step, args.steps, torch)
     scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB > L2 + MALL
     cold = time_per_step(step, args.steps, torch, scrub)
     del scrub
-    floor = read_floor_gbps(torch)
     layer_us = ms * 1000.0
     ab = algorithmic_bytes(wl, step.row_len_host)
     total_bytes = sum(ab.values())
@@ -447,8 +474,9 @@ def main(argv=None):
             "indexer_block_rows": block_rows,
             "attention_merge": "fused" if step.fused else "separate",
             "launch": "graph replay" if args.graph else "stream",
-            "topk_mode": (f"two-stage, {step.topk_chunk}-position segments" if step.topk_chunk
-                     else "one pass"),
+            "topk_mode": ("from the indexer's score histogram" if step.use_hist else
+                          f"two-stage, {step.topk_chunk}-position segments" if step.topk_chunk
+                          else "one pass"),
             "score_rows_per_window": step.window_rows,
         },
         "hbm_gbps": round(gbps, 1),
@@ -460,6 +488,7 @@ def main(argv=None):
                      "p90": round(_pct(cold, 0.9), 2),
                      "note": "a 1 GiB buffer is read before each step, outside its events"},
         },
+        "timed_steps_us": trace,
         "read_floor_gbps": round(floor, 1),
         "layer_frac_of_read_floor": round(gbps / floor, 4),
         "algorithmic_bytes": total_bytes,
@@ -478,7 +507,7 @@ def main(argv=None):
     if args.cpu_seconds > 0:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds, torch)
-    names = [n for n in args.configs.split(",") if n and n != args.workload]
+    names = [n for n in args.configs.split(",") if n and n != args.workload + ("+hist" if args.hist else "")]
     if names:
         del step, inp, graph
         torch.cuda.empty_cache()

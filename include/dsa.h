@@ -160,6 +160,45 @@ int dsa_indexer_scores_total(const void* q_idx, const float* w, const void* k_id
                              void* stream);
 
 /* ------------------------------------------------------------------------
+ * Score histograms for the selection's threshold.
+ *
+ * Commit "When a step's context bound reaches 64K keys, each row now
+ * thresholds at a sampled score ...": each row gets a threshold, a filter
+ * keeps the keys reaching it, and the exact top k is taken among those
+ * candidates. Here the threshold is exact: the histogram of a row's scores
+ * over the top 12 bits of their order keys, where the order key of a float32
+ * score x (-0.0 taken as +0.0) is bits(x) ^ 0xFFFFFFFF for x < 0 and
+ * bits(x) | 0x80000000 otherwise (unsigned order of keys = order of scores),
+ * and
+ *
+ *   hist[r][b] = #{ s < row_len[r] : order_key(scores[r][s]) >> 20 == b },
+ *
+ * b in [0, 4096). The bin where the count from the top first reaches k holds
+ * the k-th largest score, so every key of a higher bin is selected and only
+ * that bin's keys need ranking.
+ * ------------------------------------------------------------------------ */
+
+/* dsa_indexer_scores_total that also adds each row's score histogram to
+ * hist (device uint32 [rows][4096], 16-byte aligned), which must be all zero
+ * on entry -- as dsa_topk_hist leaves it (allocate it zeroed once). Decode
+ * batches count their scores inside the scoring kernel; rows of multi-row
+ * score blocks and fp32 inputs are counted by one more launch over the
+ * written scores. Errors as dsa_indexer_scores_total; NULL hist:
+ * DSA_ERR_NULL. */
+int dsa_indexer_scores_hist(const void* q_idx, const float* w, const void* k_idx_cache,
+                            const int32_t* block_table, const int32_t* row_req,
+                            const int32_t* row_len, const int32_t* blocks, int num_blocks,
+                            float* scores, uint32_t* hist, int rows, int width, int num_heads,
+                            int head_dim, int page_size, int max_pages, dsa_dtype dtype,
+                            long long total_keys, void* stream);
+
+/* dsa_score_hist: writes the histogram above of the scores already in
+ * scores (device float32 [rows][width]) to hist (device uint32
+ * [rows][4096], 16-byte aligned; cleared first, then counted). */
+int dsa_score_hist(const float* scores, const int32_t* row_len, int rows, int width,
+                   uint32_t* hist, void* stream);
+
+/* ------------------------------------------------------------------------
  * dsa_topk -- length-bounded exact top-k.
  *
  * Commits "Replace the CuTe decode kernels with two Triton kernels" (the
@@ -190,6 +229,22 @@ int dsa_topk(const float* scores, const int32_t* row_len, int rows, int width, i
  * [0, rows * width]: DSA_ERR_SHAPE. */
 int dsa_topk_total(const float* scores, const int32_t* row_len, int rows, int width, int k,
                    long long total_keys, int32_t* idx, void* stream);
+
+/* dsa_topk from the rows' score histograms (dsa_indexer_scores_hist or
+ * dsa_score_hist for these scores): the threshold bin comes from hist, the
+ * keys at or above it are compacted in position order into on-chip memory
+ * (after further radix passes over the row while they would not fit), and
+ * the selection is finished among them -- a long row is read once or twice
+ * instead of once per radix pass. The indices equal dsa_topk's bit for bit;
+ * hist is left all zero for the next step. A histogram that does not count
+ * the row's row_len scores makes the row ranked from scratch (still exact).
+ *
+ *   hist  device uint32 [rows][4096], 16-byte aligned (read, then cleared)
+ *   total_keys  as for dsa_topk_total
+ *
+ * Errors as dsa_topk_total; NULL hist: DSA_ERR_NULL. */
+int dsa_topk_hist(const float* scores, const int32_t* row_len, uint32_t* hist, int rows,
+                  int width, int k, long long total_keys, int32_t* idx, void* stream);
 
 /* ------------------------------------------------------------------------
  * dsa_topk_chunked -- the same selection as dsa_topk, in two stages.

@@ -55,6 +55,8 @@ __all__ = [
     "indexer_scores",
     "topk_row",
     "topk",
+    "order_keys",
+    "score_histogram_row",
     "split_bounds",
     "attention_split_row",
     "attention_row",
@@ -177,6 +179,40 @@ def topk(scores_rows, row_len, k):
     """Top-k of every row: int32 [rows][k]."""
     return np.stack([topk_row(s, L, k) for s, L in zip(scores_rows, row_len)]) \
         if len(scores_rows) else np.zeros((0, int(k)), np.int32)
+
+
+# --------------------------------------------------------------------------
+# Score histogram (the selection's exact threshold)
+# --------------------------------------------------------------------------
+
+
+def order_keys(scores):
+    """Order-preserving unsigned 32-bit keys of float32 scores, as int64.
+
+    IEEE-754 binary32: a non-negative value's bit pattern grows with the
+    value, a negative value's shrinks. Setting the sign bit of non-negative
+    patterns and inverting negative ones maps every float32 (-0.0 first made
+    +0.0, so the two zeros share a key) to an unsigned integer in the same
+    order as the values.
+    """
+    u = np.asarray(scores, np.float32).view(np.uint32).astype(np.int64)
+    u = np.where(u == 0x80000000, 0, u)
+    return np.where(u >= 0x80000000, 0xFFFFFFFF - u, u + 0x80000000)
+
+
+def score_histogram_row(scores, length, bits=12):
+    """Counts of a row's first ``length`` scores by the top ``bits`` bits of
+    their order keys: int64 [2**bits].
+
+    Commit "When a step's context bound reaches 64K keys, each row now
+    thresholds at a sampled score ..." thresholds every row before the exact
+    selection; this is the exact counterpart the library uses instead of a
+    sample: the bin where the count from the top first reaches k holds the
+    k-th largest score (keys of one bin are contiguous in value order).
+    """
+    length = int(length)
+    keys = order_keys(np.asarray(scores, np.float32)[:length])
+    return np.bincount(keys >> (32 - int(bits)), minlength=1 << int(bits))
 
 
 # --------------------------------------------------------------------------

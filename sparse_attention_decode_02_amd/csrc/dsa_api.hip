@@ -75,16 +75,19 @@ hipError_t indexer_launch(const void* q_idx, const float* w, const void* k_idx_c
                           const int32_t* row_len, const int32_t* blocks, int num_blocks,
                           float* scores, int rows, int width, int num_heads, int head_dim,
                           int page_shift, int max_pages, dsa_dtype dtype, bool full,
-                          hipStream_t st, int score_row0 = 0) {
+                          hipStream_t st, int score_row0 = 0, uint32_t* hist = nullptr) {
   const int nb = blocks ? num_blocks : rows;
   if (dtype == DSA_BF16)
     return dsa::launch_indexer_bf16(q_idx, w, k_idx_cache, block_table, row_req, row_len, blocks,
                                     nb, rows, scores, width, num_heads, head_dim, page_shift,
-                                    max_pages, full, score_row0, st);
-  return dsa::launch_indexer_f32(static_cast<const float*>(q_idx), w,
-                                 static_cast<const float*>(k_idx_cache), block_table, row_req,
-                                 row_len, blocks, nb, scores, width, num_heads, head_dim,
-                                 page_shift, max_pages, score_row0, st);
+                                    max_pages, full, score_row0, st, hist);
+  hipError_t e = dsa::launch_indexer_f32(static_cast<const float*>(q_idx), w,
+                                         static_cast<const float*>(k_idx_cache), block_table,
+                                         row_req, row_len, blocks, nb, scores, width, num_heads,
+                                         head_dim, page_shift, max_pages, score_row0, st);
+  if (e == hipSuccess && hist)
+    e = dsa::launch_score_hist(scores, row_len, rows, width, hist, false, st);
+  return e;
 }
 
 int topk_check(const float* scores, const int32_t* row_len, int rows, int width, int k,
@@ -180,6 +183,28 @@ int dsa_indexer_scores_total(const void* q_idx, const float* w, const void* k_id
                                       static_cast<hipStream_t>(stream)));
 }
 
+int dsa_indexer_scores_hist(const void* q_idx, const float* w, const void* k_idx_cache,
+                            const int32_t* block_table, const int32_t* row_req,
+                            const int32_t* row_len, const int32_t* blocks, int num_blocks,
+                            float* scores, uint32_t* hist, int rows, int width, int num_heads,
+                            int head_dim, int page_size, int max_pages, dsa_dtype dtype,
+                            long long total_keys, void* stream) {
+  if (!hist) return DSA_ERR_NULL;
+  if (!aligned(hist, 16)) return DSA_ERR_ALIGN;
+  if (total_keys < 0 || total_keys > (long long)rows * width) return DSA_ERR_SHAPE;
+  const bool full = rows > 0 && total_keys * 10 >= (long long)rows * width * 9;
+  int ps = 0;
+  const int st = indexer_check(q_idx, w, k_idx_cache, block_table, row_req, row_len, blocks,
+                               num_blocks, scores, rows, width, num_heads, head_dim, page_size,
+                               max_pages, dtype, full, &ps);
+  if (st != DSA_OK) return st;
+  if (rows == 0) return DSA_OK;
+  return launch_status(indexer_launch(q_idx, w, k_idx_cache, block_table, row_req, row_len,
+                                      blocks, num_blocks, scores, rows, width, num_heads,
+                                      head_dim, ps, max_pages, dtype, full,
+                                      static_cast<hipStream_t>(stream), 0, hist));
+}
+
 int dsa_indexer_scores(const void* q_idx, const float* w, const void* k_idx_cache,
                        const int32_t* block_table, const int32_t* row_req, const int32_t* row_len,
                        const int32_t* blocks, int num_blocks, float* scores, int rows, int width,
@@ -207,6 +232,29 @@ int dsa_topk_total(const float* scores, const int32_t* row_len, int rows, int wi
   if (rows == 0) return DSA_OK;
   return launch_status(dsa::launch_topk(scores, row_len, rows, width, k, idx,
                                         static_cast<hipStream_t>(stream), total_keys));
+}
+
+int dsa_topk_hist(const float* scores, const int32_t* row_len, uint32_t* hist, int rows,
+                  int width, int k, long long total_keys, int32_t* idx, void* stream) {
+  if (total_keys < 0 || total_keys > (long long)rows * width) return DSA_ERR_SHAPE;
+  const int st = topk_check(scores, row_len, rows, width, k, idx);
+  if (st != DSA_OK) return st;
+  if (!hist) return DSA_ERR_NULL;
+  if (!aligned(hist, 16)) return DSA_ERR_ALIGN;
+  if (rows == 0) return DSA_OK;
+  return launch_status(dsa::launch_topk_hist(scores, row_len, hist, rows, width, k, idx,
+                                             static_cast<hipStream_t>(stream), total_keys));
+}
+
+int dsa_score_hist(const float* scores, const int32_t* row_len, int rows, int width,
+                   uint32_t* hist, void* stream) {
+  if (!scores || !row_len || !hist) return DSA_ERR_NULL;
+  if (rows < 0 || width < 1) return DSA_ERR_SHAPE;
+  if ((long long)rows * ((width + 8191) / 8192) > INT32_MAX) return DSA_ERR_SHAPE;
+  if (!aligned(scores, 4) || !aligned(row_len, 4) || !aligned(hist, 16)) return DSA_ERR_ALIGN;
+  if (rows == 0) return DSA_OK;
+  return launch_status(dsa::launch_score_hist(scores, row_len, rows, width, hist, true,
+                                              static_cast<hipStream_t>(stream)));
 }
 
 int dsa_topk_chunked_slots(int rows, int width, int k, int chunk, long long* slots) {

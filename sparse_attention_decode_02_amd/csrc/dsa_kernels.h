@@ -31,7 +31,8 @@ hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kc
                                const int32_t* bt, const int32_t* row_req, const int32_t* row_len,
                                const int32_t* blocks, int num_blocks, int rows, float* scores,
                                int width, int num_heads, int head_dim, int page_shift,
-                               int max_pages, bool full, int score_row0, hipStream_t stream);
+                               int max_pages, bool full, int score_row0, hipStream_t stream,
+                               uint32_t* hist = nullptr);
 
 hipError_t launch_indexer_f32(const float* q_idx, const float* w, const float* kcache,
                               const int32_t* bt, const int32_t* row_req, const int32_t* row_len,
@@ -50,6 +51,17 @@ int topk_suggest_chunk(int rows, int width, int k, bool full);
 // each row's top-k over them into idx. Requires seg >= k.
 hipError_t launch_topk_chunked(const float* scores, const int32_t* row_len, int rows, int width,
                                int k, int seg, int32_t* cand, int32_t* idx, hipStream_t stream);
+
+// Histogram-driven exact top-k: hist [rows][4096] counts each row's scores
+// by the top 12 bits of their order keys (as the indexer leaves it); the
+// selection equals launch_topk's and hist is left cleared.
+hipError_t launch_topk_hist(const float* scores, const int32_t* row_len, uint32_t* hist, int rows,
+                            int width, int k, int32_t* idx, hipStream_t stream,
+                            long long total_keys = 0);
+// Adds each row's score counts to hist [rows][4096] (cleared first when
+// `clear`), from the scores already written.
+hipError_t launch_score_hist(const float* scores, const int32_t* row_len, int rows, int width,
+                             uint32_t* hist, bool clear, hipStream_t stream);
 
 hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, const int32_t* bt,
                               const int32_t* row_req, const int32_t* idx, int rows, int hq,

@@ -30,7 +30,7 @@
 // keys cross HBM/L2 once per block rather than once per row and the
 // contraction runs on the matrix cores at prefill's arithmetic intensity.
 
-#include "dsa_kernels.h"
+#include "radix_select.h"
 
 namespace dsa {
 
@@ -80,11 +80,15 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_mfma_kernel(
     const uint16_t* __restrict__ kc, const int32_t* __restrict__ bt,
     const int32_t* __restrict__ row_req, const int32_t* __restrict__ row_len,
     const int32_t* __restrict__ blocks, float* __restrict__ scores, int width, int page_shift,
-    int max_pages, int chunk_keys, int chunks, int total, int score_row0, int single_only) {
+    int max_pages, int chunk_keys, int chunks, int total, int score_row0, int single_only,
+    uint32_t* __restrict__ hist) {
   constexpr int H = HT * 16;
   constexpr int KS = DI / 32;  // MFMA steps per head tile
   constexpr int QST = DI + 8;  // padded LDS row (elements): the 16 rows read together hit distinct banks
   __shared__ __attribute__((aligned(16))) uint16_t q_lds[H * QST];
+  // The chunk's score histogram (with `hist`): two 16-bit counters per word
+  // (a chunk holds at most 2048 keys), bins 2i and 2i + 1 in word i.
+  __shared__ uint32_t h_lds[kHistBins / 2];
   __shared__ __attribute__((aligned(16))) float w_lds[H];
   __shared__ __attribute__((aligned(16))) float s_lds[kMaxChunkKeys];  // the chunk's scores
 
@@ -160,6 +164,8 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_mfma_kernel(
         *reinterpret_cast<uint4*>(&q_lds[h * QST + c * 8]) = qreg[i];
       }
       if (tid < H) w_lds[tid] = wv_;
+      if (hist)
+        for (int i = tid; i < kHistBins / 2; i += kIdxThreads) h_lds[i] = 0u;
     }
     __syncthreads();
 
@@ -187,9 +193,16 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_mfma_kernel(
         part = fmaf(wr[t].z, relu(acc[2]), part);
         part = fmaf(wr[t].w, relu(acc[3]), part);
       }
-      part = sum_rows(part);
+      part = sum_rows(part) + 0.0f;
       const int s = base + kl;
-      if (grp == 0 && s < L) s_lds[s - chunk0] = part + 0.0f;
+      if (grp == 0 && s < L) {
+        s_lds[s - chunk0] = part;
+        if (hist) {
+          // Counted as it is made, under the key loads in flight.
+          const uint32_t bin = order_key(part) >> kHistShift;
+          atomicAdd(&h_lds[bin >> 1], 1u << ((bin & 1u) << 4));
+        }
+      }
     };
 
     // kKeyBufs key-fragment buffers in rotation: while one tile runs on the
@@ -215,6 +228,18 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_mfma_kernel(
                                     reinterpret_cast<f32x4v*>(out + chunk0 + i));
       } else {
         for (int j = i; j < nk; ++j) out[chunk0 + j] = s_lds[j];
+      }
+    }
+    if (hist) {
+      // The chunk's counts (the selection's threshold histogram: scores by
+      // the top 12 bits of their order keys) join the row's: one global
+      // atomic per non-empty bin. The next row clears h_lds only after a
+      // barrier.
+      uint32_t* hr = hist + (size_t)(r - score_row0) * kHistBins;
+      for (int i = tid; i < kHistBins / 2; i += kIdxThreads) {
+        const uint32_t n = h_lds[i];
+        if (n & 0xFFFFu) atomicAdd(&hr[2 * i], n & 0xFFFFu);
+        if (n >> 16) atomicAdd(&hr[2 * i + 1], n >> 16);
       }
     }
   }
@@ -508,7 +533,8 @@ hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kc
                                const int32_t* bt, const int32_t* row_req, const int32_t* row_len,
                                const int32_t* blocks, int num_blocks, int rows, float* scores,
                                int width, int num_heads, int head_dim, int page_shift,
-                               int max_pages, bool full, int score_row0, hipStream_t stream) {
+                               int max_pages, bool full, int score_row0, hipStream_t stream,
+                               uint32_t* hist) {
   const auto* q = static_cast<const uint16_t*>(q_idx);
   const auto* k = static_cast<const uint16_t*>(kcache);
   const bool with_block_kernel = blocks && indexer_uses_blocks(rows, num_blocks);
@@ -538,14 +564,19 @@ hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kc
                      dim3(single_only ? xcd_grouped_grid(total, 2) : total), dim3(kIdxThreads), 0, \
                      stream,                                                                   \
                      q, w, k, bt, row_req, row_len, blocks, scores, width, page_shift,         \
-                     max_pages, chunk, chunks, total, score_row0, single_only)
+                     max_pages, chunk, chunks, total, score_row0, single_only,                 \
+                     with_block_kernel ? nullptr : hist)
   if (num_heads == 64 && head_dim == 128) DSA_IDX_LAUNCH(4, 128);
   else if (num_heads == 32 && head_dim == 128) DSA_IDX_LAUNCH(2, 128);
   else if (num_heads == 64 && head_dim == 64) DSA_IDX_LAUNCH(4, 64);
   else if (num_heads == 32 && head_dim == 64) DSA_IDX_LAUNCH(2, 64);
   else return hipErrorInvalidValue;
 #undef DSA_IDX_LAUNCH
-  return hipGetLastError();
+  hipError_t e = hipGetLastError();
+  // Rows scored by the block kernel are counted from their written scores.
+  if (e == hipSuccess && hist && with_block_kernel)
+    e = launch_score_hist(scores, row_len, rows, width, hist, false, stream);
+  return e;
 }
 
 hipError_t launch_indexer_f32(const float* q_idx, const float* w, const float* kcache,

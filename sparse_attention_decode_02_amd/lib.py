@@ -41,6 +41,10 @@ _SIGS = {
     "dsa_indexer_scores": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I, _P]),
     "dsa_indexer_scores_total": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _I, _I, _I, _I, _I, _I, _I,
                                       _LL, _P]),
+    "dsa_indexer_scores_hist": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _P, _P, _I, _I, _I, _I, _I, _I,
+                                     _I, _LL, _P]),
+    "dsa_score_hist": (_I, [_P, _P, _I, _I, _P, _P]),
+    "dsa_topk_hist": (_I, [_P, _P, _P, _I, _I, _I, _LL, _P, _P]),
     "dsa_topk": (_I, [_P, _P, _I, _I, _I, _P, _P]),
     "dsa_topk_total": (_I, [_P, _P, _I, _I, _I, _LL, _P, _P]),
     "dsa_topk_chunked": (_I, [_P, _P, _I, _I, _I, _I, _P, _LL, _P, _P]),
@@ -206,6 +210,50 @@ def indexer_scores(q_idx, w, k_idx_cache, block_table, row_req, row_len, scores,
     else:
         p = _call("dsa_indexer_scores_total", args + [int(total_keys)], stream, prepare)
     return p if prepare else scores
+
+
+HIST_BINS = 4096  # bins of a score histogram: the top 12 bits of the order key
+
+
+def indexer_scores_hist(q_idx, w, k_idx_cache, block_table, row_req, row_len, scores, hist,
+                        page_size, blocks=None, stream=None, total_keys=0, prepare=False):
+    """dsa_indexer_scores_hist: the scores, and each row's score histogram
+    added to hist [rows][4096] uint32 (which must be zero on entry)."""
+    rows, heads, dim = q_idx.shape
+    dt = _dtype_code(q_idx)
+    if k_idx_cache.dtype != q_idx.dtype:
+        raise TypeError("q_idx and k_idx_cache dtypes differ")
+    if hist.dtype != torch.int32 and hist.dtype != torch.uint32:
+        raise TypeError("hist must be a 32-bit integer tensor")
+    nb = 0 if blocks is None else int(blocks.shape[0])
+    p = _call("dsa_indexer_scores_hist", [
+        _dev(q_idx, "q_idx"), _dev(w, "w", torch.float32), _dev(k_idx_cache, "k_idx_cache"),
+        _dev(block_table, "block_table", torch.int32), _dev(row_req, "row_req", torch.int32),
+        _dev(row_len, "row_len", torch.int32),
+        None if blocks is None else _dev(blocks, "blocks", torch.int32), nb,
+        _dev(scores, "scores", torch.float32), _dev(hist, "hist"), rows, int(scores.shape[1]),
+        heads, dim, int(page_size), int(block_table.shape[1]), dt, int(total_keys)], stream, prepare)
+    return p if prepare else scores
+
+
+def score_hist(scores, row_len, hist, stream=None):
+    """dsa_score_hist: hist [rows][4096] of the scores already written."""
+    rows, width = scores.shape
+    _call("dsa_score_hist", [_dev(scores, "scores", torch.float32),
+                             _dev(row_len, "row_len", torch.int32), rows, width,
+                             _dev(hist, "hist")], stream, False)
+    return hist
+
+
+def topk_hist(scores, row_len, hist, k, idx, stream=None, total_keys=0, prepare=False):
+    """dsa_topk_hist: dsa_topk from the rows' score histograms (hist is left
+    zero); writes idx [rows][k] in place."""
+    rows, width = scores.shape
+    p = _call("dsa_topk_hist", [
+        _dev(scores, "scores", torch.float32), _dev(row_len, "row_len", torch.int32),
+        _dev(hist, "hist"), rows, width, int(k), int(total_keys), _dev(idx, "idx", torch.int32)],
+        stream, prepare)
+    return p if prepare else idx
 
 
 def topk(scores, row_len, k, idx, stream=None, total_keys=None, prepare=False):

@@ -28,11 +28,15 @@ class DsaStep:
     takes the library's suggestion for the sizes, 0 the one-pass kernel.
     ``score_buffer_bytes`` bounds the score memory: rows are scored and
     selected in windows that fit it (dsa_indexer_topk_windowed), and
-    ``scores`` then holds only the last window's rows."""
+    ``scores`` then holds only the last window's rows. ``hist`` has the
+    indexer count each row's scores by the top bits of their order keys
+    (dsa_indexer_scores_hist) and the top-k start from those counts
+    (dsa_topk_hist), which leaves them cleared for the next run; it excludes
+    score windows and the two-stage top-k."""
 
     def __init__(self, inp, num_splits: int | None = None, block_rows: int = 1,
                  fused: bool | None = False, topk_chunk: int | None = 0,
-                 score_buffer_bytes: int | None = None):
+                 score_buffer_bytes: int | None = None, hist: bool = False):
         wl = inp.wl
         dev = inp.q.device
         self.inp = inp
@@ -59,6 +63,11 @@ class DsaStep:
         self.window_rows = self.rows
         if score_buffer_bytes is not None:
             self.window_rows = min(self.rows, lib.select_window_rows(self.width, score_buffer_bytes))
+        self.use_hist = hist
+        if hist and (score_buffer_bytes is not None or topk_chunk):
+            raise ValueError("the histogram top-k does not combine with score windows or two stages")
+        if hist:
+            topk_chunk = 0
         if topk_chunk is None:
             # The suggestion for a window's rows, at the batch's fill.
             window_keys = self.total_keys * self.window_rows // max(1, self.rows)
@@ -78,6 +87,9 @@ class DsaStep:
                                     device=dev)
         self.out = torch.empty(self.rows, wl.hq, wl.d, dtype=inp.q.dtype, device=dev)
         self.out_lse = torch.empty(self.rows, wl.hq, dtype=torch.float32, device=dev)
+        # Zero once; the top-k clears the counts it read.
+        self.hist = (torch.zeros(self.rows, lib.HIST_BINS, dtype=torch.int32, device=dev)
+                     if hist else None)
 
         self._prepare()
 
@@ -93,6 +105,12 @@ class DsaStep:
                 i.qI, i.w, i.kI_cache, i.block_table, self.row_req, self.row_len, self.width,
                 wl.page, wl.topk, self.scores, self.idx, topk_chunk=self.topk_chunk,
                 cand=self.cand, prepare=True, blocks=self.blocks, blocks_host=self.blocks_host)
+        elif self.use_hist:
+            self._calls["indexer"] = lib.indexer_scores_hist(
+                i.qI, i.w, i.kI_cache, i.block_table, self.row_req, self.row_len, self.scores,
+                self.hist, wl.page, blocks=self.blocks, total_keys=self.total_keys, prepare=True)
+            self._calls["topk"] = lib.topk_hist(self.scores, self.row_len, self.hist, wl.topk,
+                                                self.idx, total_keys=self.total_keys, prepare=True)
         else:
             self._calls["indexer"] = lib.indexer_scores(
                 i.qI, i.w, i.kI_cache, i.block_table, self.row_req, self.row_len, self.scores,

@@ -20,8 +20,8 @@ CANARY = 0x7FBADBAD  # a NaN bit pattern pre-filled into the score buffer
 TOL = {"bf16": (2e-2, 1e-3), "f32": (1e-5, 1e-5)}
 
 
-def run_step(inp, num_splits=None, block_rows=1, canary=True, fused=False):
-    step = DsaStep(inp, num_splits=num_splits, block_rows=block_rows, fused=fused)
+def run_step(inp, num_splits=None, block_rows=1, canary=True, fused=False, hist=False, **kw):
+    step = DsaStep(inp, num_splits=num_splits, block_rows=block_rows, fused=fused, hist=hist, **kw)
     if canary:
         step.scores.view(torch.int32).fill_(CANARY)
     step.run()

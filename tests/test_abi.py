@@ -223,6 +223,43 @@ def test_topk_chunked_noalloc_limit():
     assert lib.topk_chunked_slots(64, 204800, 2048, 32768) <= lib.TOPK_NOALLOC_MAX_SLOTS
 
 
+def _topk_hist_args(**kw):
+    a = dict(scores=A, row_len=A, hist=A, rows=4, width=128, k=16, total=0, idx=A, stream=None)
+    a.update(kw)
+    return list(a.values())
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hist=None), NULL), (dict(scores=None), NULL), (dict(idx=None), NULL),
+    (dict(hist=A + 4), ALIGN), (dict(k=0), SHAPE), (dict(k=129), SHAPE), (dict(width=66), SHAPE),
+    (dict(total=-1), SHAPE), (dict(total=4 * 128 + 1), SHAPE), (dict(rows=0), OK),
+])
+def test_topk_hist_rejects(kw, code):
+    assert lib._lib.dsa_topk_hist(*_topk_hist_args(**kw)) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hist=None), NULL), (dict(scores=None), NULL), (dict(hist=A + 8), ALIGN),
+    (dict(row_len=A + 2), ALIGN), (dict(rows=-1), SHAPE), (dict(width=0), SHAPE), (dict(rows=0), OK),
+])
+def test_score_hist_rejects(kw, code):
+    a = dict(scores=A, row_len=A, rows=4, width=128, hist=A, stream=None)
+    a.update(kw)
+    assert lib._lib.dsa_score_hist(*a.values()) == code
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(hist=None), NULL), (dict(hist=A + 4), ALIGN), (dict(total=-1), SHAPE),
+    (dict(q_idx=None), NULL), (dict(head_dim=96), UNSUP), (dict(rows=0, total=0), OK),
+])
+def test_indexer_scores_hist_rejects(kw, code):
+    a = dict(q_idx=A, w=A, k_idx_cache=A, block_table=A, row_req=A, row_len=A, blocks=None,
+             num_blocks=0, scores=A, hist=A, rows=4, width=128, num_heads=64, head_dim=128,
+             page_size=64, max_pages=2, dtype=1, total=0, stream=None)
+    a.update(kw)
+    assert lib._lib.dsa_indexer_scores_hist(*a.values()) == code
+
+
 def test_topk_chunked_slots():
     assert lib.topk_chunked_slots(4, 128, 16, 32) == 2 * 4 * 4 * 16
     assert lib.topk_chunked_slots(4, 132, 16, 32) == 2 * 4 * 5 * 16

@@ -426,3 +426,67 @@ def test_layer_row_tiny_workload_consistency():
         o1, l1 = O.attention_row(I.as_f64(inp.q)[r], I.as_f64(inp.k_cache), I.as_f64(inp.v_cache),
                                  inp.block_table.numpy()[req[r]], wl.page, idx, wl.attn_scale)
         np.testing.assert_allclose(o, o1, rtol=0, atol=1e-12)
+
+
+# --------------------------------------------------------------------------
+# Score histogram (the selection's exact threshold)
+# --------------------------------------------------------------------------
+
+
+def test_golden_order_key_bins(golden):
+    g = golden["order_key_bins"]["cases"]
+    sc = np.asarray([_f(c["score"]) for c in g], np.float32)
+    keys = O.order_keys(sc)
+    assert keys.tolist() == [c["key"] for c in g]
+    h = O.score_histogram_row(sc, len(sc))
+    want = np.zeros(4096, np.int64)
+    for c in g:
+        want[c["bin"]] += 1
+    assert np.array_equal(h, want)
+
+
+def test_order_keys_brute_force():
+    """Each key from the bit pattern, one value at a time (struct), and the
+    key order equals the value order over all kinds of float32."""
+    import struct
+    rng = np.random.default_rng(4)
+    vals = np.concatenate([
+        rng.standard_normal(200) * 10.0 ** rng.integers(-40, 38, 200),
+        [0.0, -0.0, np.inf, -np.inf, 1e-45, -1e-45, 3.4e38, -3.4e38, 1.0, -1.0],
+        np.round(rng.normal(2240, 400, 100) * 2) / 2]).astype(np.float32)
+    for v in vals:
+        b = struct.unpack("<I", struct.pack("<f", float(v)))[0]
+        if b == 0x80000000:
+            b = 0
+        want = (b ^ 0xFFFFFFFF) if b >> 31 else (b | 0x80000000)
+        assert int(O.order_keys(np.asarray([v], np.float32))[0]) == want
+    order = np.argsort(vals.astype(np.float64), kind="stable")
+    k = O.order_keys(vals)[order]
+    assert np.all(np.diff(k) >= 0)
+    eq = np.diff(vals.astype(np.float64)[order]) == 0
+    assert np.all((np.diff(k) == 0) == eq)
+
+
+@pytest.mark.parametrize("seed", range(6))
+def test_score_histogram_threshold_bin(seed):
+    """The histogram counts exactly the row's first L scores, and the bin
+    where the count from the top reaches k holds the k-th largest score -- the
+    smallest score the top-k selects."""
+    rng = np.random.default_rng(seed)
+    L = int(rng.integers(1, 5000))
+    width = L + int(rng.integers(0, 100))
+    sc = (rng.integers(-50, 400, width) / 4).astype(np.float32)
+    sc[L:] = np.nan
+    h = O.score_histogram_row(sc, L)
+    assert int(h.sum()) == L
+    brute = np.zeros(4096, np.int64)
+    for v in sc[:L]:
+        brute[int(O.order_keys(np.asarray([v], np.float32))[0]) >> 20] += 1
+    assert np.array_equal(h, brute)
+    for k in (1, 7, min(L, 100), L):
+        top = np.cumsum(h[::-1])
+        b = 4095 - int(np.argmax(top >= k))
+        sel = O.topk_row(sc, L, k)
+        kth = sc[sel[sel >= 0]].min()
+        assert int(O.order_keys(np.asarray([kth], np.float32))[0]) >> 20 == b
+        assert int(top[4095 - b]) - int(h[b]) < k <= int(top[4095 - b])

@@ -228,6 +228,105 @@ def test_topk_edges(k, copies, width):
         assert np.array_equal(got[i], want), f"{name}: first diff at {np.flatnonzero(got[i] != want)[:5]}"
 
 
+def _oracle_hist(sc, L):
+    return O.score_histogram_row(sc, L).astype(np.int64)
+
+
+@pytest.mark.parametrize("width", [70016, 16384, 4096])
+def test_score_hist_matches_oracle(width):
+    """dsa_score_hist counts every edge row's scores exactly as the oracle."""
+    from sparse_attention_decode_02_amd import lib
+    cases = [(n, sc[:width]) for n, sc in _topk_case_rows(width, 2048)]
+    scores = np.full((len(cases), width), np.nan, np.float32)
+    lens = np.zeros(len(cases), np.int32)
+    for i, (_, sc) in enumerate(cases):
+        scores[i, : len(sc)] = sc
+        lens[i] = len(sc)
+    hist = torch.full((len(cases), lib.HIST_BINS), 7, dtype=torch.int32, device="cuda")
+    lib.score_hist(torch.from_numpy(scores).cuda(), torch.from_numpy(lens).cuda(), hist)
+    got = hist.cpu().numpy().astype(np.int64)
+    for i, (name, sc) in enumerate(cases):
+        assert np.array_equal(got[i], _oracle_hist(sc, len(sc))), name
+
+
+@pytest.mark.parametrize("k", [1, 16, 2048])
+@pytest.mark.parametrize("copies,width", [(1, 70016), (13, 70016), (1, 4096), (1, 8192), (3, 16384)],
+                         ids=["few-rows", "many-rows", "w4096", "w8192", "w16384"])
+def test_topk_hist_edges(k, copies, width):
+    """The histogram-driven selection on every edge row against the oracle;
+    the histogram comes back cleared. Rows whose candidates overflow the
+    on-chip list (long fully tied rows) take the narrowing passes and the
+    emit over the row."""
+    from sparse_attention_decode_02_amd import lib
+    if k > width:
+        pytest.skip("k > width")
+    cases = [(n, sc[:width]) for n, sc in _topk_case_rows(width, k)] * copies
+    _say(f"histogram top-k edges, k {k}, {len(cases)} rows")
+    scores = np.full((len(cases), width), np.nan, np.float32)
+    lens = np.zeros(len(cases), np.int32)
+    for i, (_, sc) in enumerate(cases):
+        scores[i, : len(sc)] = sc
+        lens[i] = len(sc)
+    s_d = torch.from_numpy(scores).cuda()
+    l_d = torch.from_numpy(lens).cuda()
+    hist = torch.zeros((len(cases), lib.HIST_BINS), dtype=torch.int32, device="cuda")
+    lib.score_hist(s_d, l_d, hist)
+    idx = torch.full((len(cases), k), -7, dtype=torch.int32, device="cuda")
+    lib.topk_hist(s_d, l_d, hist, k, idx, total_keys=int(lens.astype(np.int64).sum()))
+    torch.cuda.synchronize()
+    assert not bool(hist.any()), "the histogram was not cleared"
+    got = idx.cpu().numpy()
+    for i, (name, sc) in enumerate(cases):
+        want = O.topk_row(sc, len(sc), k)
+        assert np.array_equal(got[i], want), f"{name}: first diff at {np.flatnonzero(got[i] != want)[:5]}"
+
+
+def test_topk_hist_without_a_matching_histogram():
+    """A histogram that does not count the row (here all zero) makes the
+    selection rank the row from scratch: still the oracle's indices."""
+    from sparse_attention_decode_02_amd import lib
+    cases, s_d, l_d = _edge_batch(2048)
+    hist = torch.zeros((len(cases), lib.HIST_BINS), dtype=torch.int32, device="cuda")
+    idx = torch.full((len(cases), 2048), -7, dtype=torch.int32, device="cuda")
+    lib.topk_hist(s_d, l_d, hist, 2048, idx)
+    torch.cuda.synchronize()
+    got = idx.cpu().numpy()
+    for i, (name, sc) in enumerate(cases):
+        assert np.array_equal(got[i], O.topk_row(sc, len(sc), 2048)), name
+
+
+@pytest.mark.parametrize("wl_fn,block_rows", [(I.decode, 1), (lambda: _small_mixed(seed=43), 8),
+                                              (lambda: _small_mixed(seed=44), 1), (I.tiny, 1)],
+                         ids=["decode", "blocks", "small-mixed", "tiny-f32"])
+def test_indexer_hist_and_step(wl_fn, block_rows):
+    """dsa_indexer_scores_hist leaves the oracle's histogram of every row
+    (fused in the row kernel, counted after the block kernel or the fp32
+    kernel), and the histogram step gives the default step's bits."""
+    inp = _host_inputs(wl_fn())
+    ref = run_step(inp, block_rows=block_rows, fused=None)
+    step = DsaStep(inp, block_rows=block_rows, fused=None, hist=True)
+    step.scores.view(torch.int32).fill_(CANARY)
+    step.indexer()
+    torch.cuda.synchronize()
+    h = step.hist.cpu().numpy().astype(np.int64)
+    for r in range(step.rows):
+        L = int(step.row_len_host[r])
+        sc = step.scores[r, :L].cpu().numpy()
+        assert np.array_equal(h[r], _oracle_hist(sc, L)), r
+    step.topk()
+    step.attention()
+    step.merge()
+    torch.cuda.synchronize()
+    assert not bool(step.hist.any())
+    for x, y in ((ref.idx, step.idx), (ref.out, step.out), (ref.out_lse, step.out_lse)):
+        assert torch.equal(x.view(torch.uint8), y.view(torch.uint8))
+    for r in range(0, step.rows, max(1, step.rows // 6)):
+        check_row(step, r)
+    step.run()  # a second step on the cleared counts
+    torch.cuda.synchronize()
+    assert torch.equal(ref.idx, step.idx) and not bool(step.hist.any())
+
+
 @pytest.mark.parametrize("k", [16, 2048])
 def test_topk_hint_many_short_rows(k):
     """A batch of at least four rows per CU, short on average: with the
@@ -638,7 +737,24 @@ def _same_selection_other_ways(step):
                               blocks=step.blocks, blocks_host=step.blocks_host)
     torch.cuda.synchronize()
     assert torch.equal(idx, step.idx), "windowed indexer + top-k differs"
-    _say(f"  two-stage top-k (chunk {chunk}) and {window}-row windows: identical indices")
+    del buf
+    # The histogram path: the indexer again (same scores, now with each row's
+    # counts), then the selection from the counts.
+    hist = torch.zeros(step.rows, lib.HIST_BINS, dtype=torch.int32, device="cuda")
+    ref_scores_sum = float(step.scores[0, : int(step.row_len_host[0])].double().sum())
+    lib.indexer_scores_hist(inp.qI, inp.w, inp.kI_cache, inp.block_table, step.row_req,
+                            step.row_len, step.scores, hist, wl.page, blocks=step.blocks,
+                            total_keys=step.total_keys)
+    torch.cuda.synchronize()
+    assert float(step.scores[0, : int(step.row_len_host[0])].double().sum()) == ref_scores_sum
+    assert torch.equal(hist.sum(1, dtype=torch.int64), step.row_len.long()), "histogram counts"
+    idx.fill_(-7)
+    lib.topk_hist(step.scores, step.row_len, hist, wl.topk, idx, total_keys=step.total_keys)
+    torch.cuda.synchronize()
+    assert torch.equal(idx, step.idx), "histogram top-k differs"
+    assert not bool(hist.any())
+    _say(f"  two-stage top-k (chunk {chunk}), {window}-row windows and the histogram path: "
+         "identical indices")
 
 
 def _full(wl, rows_fn):
