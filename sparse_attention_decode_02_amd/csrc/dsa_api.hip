@@ -491,10 +491,8 @@ int dsa_read_probe(const void* src, long long bytes, float* sink, int sink_len, 
   if (!src || !sink) return DSA_ERR_NULL;
   if (bytes < 16 || (bytes & 15) != 0 || sink_len < 1) return DSA_ERR_SHAPE;
   if (!aligned(src, 16) || !aligned(sink, 4)) return DSA_ERR_ALIGN;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus = 256;
+  int cus = dsa::device_cus();
+  if (cus <= 0) cus = 256;
   const int blocks = sink_len < 8 * cus ? sink_len : 8 * cus;
   return launch_status(
       dsa::launch_read_probe(src, bytes, sink, blocks, static_cast<hipStream_t>(stream)));

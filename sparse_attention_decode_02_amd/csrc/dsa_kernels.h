@@ -10,8 +10,11 @@ namespace dsa {
 
 // Workgroups of `kernel` (launched with `block` threads) that the current
 // device runs at once: compute units x resident workgroups per unit. 0 on a
-// HIP error.
+// HIP error. Looked up once per (device, kernel, block) and kept.
 int device_capacity(const void* kernel, int block);
+// Compute units of the current device (looked up once per device); 0 on a
+// HIP error.
+int device_cus();
 
 // Keys a workgroup of the bf16 indexer covers for one row (a multiple of 64):
 // the chunks of all blocks fill the device about once, at most 2048 keys.

@@ -467,14 +467,6 @@ __global__ __launch_bounds__(kIdxThreads) void indexer_f32_kernel(
   }
 }
 
-int device_capacity(const void* kernel, int block) {
-  int dev = 0, cus = 0, per_cu = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return 0;
-  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess) return 0;
-  return cus * per_cu;
-}
-
 static const void* indexer_kernel_ptr(int num_heads, int head_dim) {
   if (num_heads == 64 && head_dim == 128) return (const void*)indexer_mfma_kernel<4, 128>;
   if (num_heads == 32 && head_dim == 128) return (const void*)indexer_mfma_kernel<2, 128>;

@@ -518,10 +518,7 @@ int merged_default_splits(int rows, int hq, int hkv, int d, int k, bool bf16) {
   // occupancy allows it); otherwise the split kernel's suggestion rounded
   // down to a supported workgroup size (1, 2, 4 or 8 waves).
   const void* kern = bf16 ? attn_kernel_ptr<uint16_t>(d, hq / hkv) : attn_kernel_ptr<float>(d, hq / hkv);
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus = 0;
+  int cus = device_cus();
   int cap = kern ? device_capacity(kern, 64) : 0;
   if (cap <= 0 || cus <= 0) {
     cus = 256;

@@ -325,10 +325,8 @@ hipError_t launch_topk(const float* scores, const int32_t* row_len, int rows, in
   // thread, which halves the chunk re-reads of rows past 32768; batches of
   // many rows fill the device either way and keep 32 (shorter rows then use
   // more of the workgroup's threads).
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus = 256;
+  int cus = device_cus();
+  if (cus <= 0) cus = 256;
   // Narrow rows: 512 threads holding up to 32 keys each. A radix pass costs
   // about the same in barriers and bin scans whatever the row length, and
   // with half the waves those fixed costs halve (batch 8, width 4096:
@@ -374,10 +372,8 @@ int topk_suggest_chunk(int rows, int width, int k, bool full) {
   // short ones) as long as its first stage stays within a few workgroups per
   // compute unit.
   constexpr int kSeg = kTopkThreads * 32;
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus = 256;
+  int cus = device_cus();
+  if (cus <= 0) cus = 256;
   if (width <= kTopkThreads * 64 || k > kSeg) return 0;
   if (full) return kSeg;
   const long long wgs = (long long)rows * topk_segments(width, kSeg);

@@ -364,10 +364,8 @@ hipError_t launch_topk_hist(const float* scores, const int32_t* row_len, uint32_
   // a row longer than the registers hold is read once more for its list
   // rather than once per radix pass, so the 64-keys-per-thread shape (which
   // would spill here) is not needed. The list holds 8 keys per thread.
-  int dev = 0, cus = 0;
-  if (hipGetDevice(&dev) != hipSuccess ||
-      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-    cus = 256;
+  int cus = device_cus();
+  if (cus <= 0) cus = 256;
   const bool many_short = total_keys > 0 && rows >= 4 * cus && total_keys <= 16384LL * rows;
 #define DSA_TOPK_HIST(T, V)                                                                    \
   hipLaunchKernelGGL((topk_hist_kernel<T, V, T * 8>), dim3(rows), dim3(T), 0, stream, scores, \
