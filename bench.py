@@ -283,11 +283,13 @@ def measure_configs(names, steps, warmup, torch):
     for spec in names:
         name, _, opt = spec.partition("+")
         hist = opt == "hist"
+        group = opt == "group"
         wl = I.WORKLOADS[name]()
-        print(f"[bench] config {wl.name}{' (histogram top-k)' if hist else ''}", file=sys.stderr,
-              flush=True)
+        print(f"[bench] config {wl.name}{' (histogram top-k)' if hist else ''}"
+              f"{' (group attention)' if group else ''}", file=sys.stderr, flush=True)
         inp = I.generate(wl, "cuda")
-        step = DsaStep(inp, block_rows=8, fused=None, topk_chunk=0 if hist else None, hist=hist)
+        step = DsaStep(inp, block_rows=8, fused=None, topk_chunk=0 if hist else None, hist=hist,
+                       group_attn=group)
         torch.cuda.synchronize()
         ms = time_steps(step, steps, warmup, torch)
         kern = time_kernels(step, max(5, steps // 4), torch)
@@ -300,6 +302,10 @@ def measure_configs(names, steps, warmup, torch):
                "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
                "kernels_us": {n: round(v, 2) for n, v in kern.items()},
                "attention_splits": step.num_splits,
+               "attention": ("prefill groups over the union of their selections (matrix "
+                             f"cores), {step.rows - step.group_rows} rows on the vector kernel"
+                             if step.groups is not None else "vector kernel, fused merge"
+                             if step.fused else "vector kernel, separate merge"),
                "topk_mode": ("from the indexer's score histogram" if step.use_hist else
                              f"two-stage, {step.topk_chunk}-position segments"
                              if step.topk_chunk else "one pass")}
@@ -375,7 +381,8 @@ def main(argv=None):
                     help="record the step into a HIP graph once and time its replays")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="oracle time budget for cpu_baseline, per core setting (0 = skip)")
-    ap.add_argument("--configs", default="tiny,decode,ragged,mixed,ragged+hist,long,long+hist",
+    ap.add_argument("--configs",
+                    default="tiny,decode,ragged,mixed,ragged+hist,mixed+group,long,long+hist",
                     help="other workloads measured in the same run (comma list, '' = none; "
                          "name+hist: with the histogram top-k)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,

@@ -422,6 +422,44 @@ int dsa_sparse_attn_merged(const void* q, const void* k_cache, const void* v_cac
                            int page_size, int max_pages, float scale, int num_splits, void* out,
                            float* out_lse, dsa_dtype dtype, void* stream);
 
+/* ------------------------------------------------------------------------
+ * dsa_group_attn -- prefill group attention over the union of selections.
+ *
+ * Commit "--dsa-inference-backend flashinfer ...": prefill tiles attend each
+ * 8-token group over the union of the keys its tokens selected, with a
+ * per-token bitmask; commit "Restore the upstream Blackwell FP32 probability
+ * reduction": probabilities stay fp32 through the value reduction. For every
+ * group g = {first_row, n_rows} (groups[g][0], groups[g][1]; 1 <= n_rows <= 8
+ * consecutive rows of one request, scored against first_row's block-table
+ * row) and each of its rows r, writes what dsa_sparse_attn with one split
+ * followed by dsa_merge writes for row r (up to rounding order):
+ *
+ *   out[r][h] = sum_j softmax_j(scale * q[r][h] . K[p_j][g]) V[p_j][g],
+ *   out_lse[r][h] = the log-sum-exp,
+ *
+ * over row r's valid selections p_j. The keys of the union are read once per
+ * group and KV head, and its 64 query rows (8 rows x 8 heads) run on the
+ * matrix cores; the fp32 probabilities enter the value product as three exact
+ * bf16 terms. Each row's valid selections must be distinct and ascending,
+ * followed by -1 padding (dsa_topk's output); rows not in any group are not
+ * written.
+ *
+ *   q, k_cache, v_cache, block_table, row_req, idx: as for dsa_sparse_attn
+ *   groups   device int32 [num_groups][2]: (first_row, n_rows), rows in
+ *            [0, rows) (a caller contract, like the score blocks)
+ *   out      device [rows][num_q_heads][128] bf16 (output, the groups' rows)
+ *   out_lse  device [rows][num_q_heads] float32 (output), or NULL
+ *
+ * Supported: bf16, head_dim 128, num_q_heads / num_kv_heads = 8; page_size a
+ * power of two; q, k_cache, v_cache 16-byte aligned. Otherwise
+ * DSA_ERR_UNSUPPORTED / DSA_ERR_SHAPE / DSA_ERR_ALIGN as for dsa_sparse_attn.
+ * ------------------------------------------------------------------------ */
+int dsa_group_attn(const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* block_table, const int32_t* row_req, const int32_t* idx,
+                   const int32_t* groups, int num_groups, int rows, int num_q_heads,
+                   int num_kv_heads, int head_dim, int k, int page_size, int max_pages,
+                   float scale, void* out, float* out_lse, dsa_dtype dtype, void* stream);
+
 /* dsa_sparse_attn_merged_splits: a num_splits for dsa_sparse_attn_merged
  * with these shapes on the current device: 6 when rows x KV groups x 6 waves
  * fill the device in about one round, else dsa_sparse_attn_splits rounded

@@ -441,6 +441,33 @@ int dsa_sparse_attn_merged(const void* q, const void* k_cache, const void* v_cac
       static_cast<hipStream_t>(stream)));
 }
 
+int dsa_group_attn(const void* q, const void* k_cache, const void* v_cache,
+                   const int32_t* block_table, const int32_t* row_req, const int32_t* idx,
+                   const int32_t* groups, int num_groups, int rows, int num_q_heads,
+                   int num_kv_heads, int head_dim, int k, int page_size, int max_pages,
+                   float scale, void* out, float* out_lse, dsa_dtype dtype, void* stream) {
+  if (!q || !k_cache || !v_cache || !block_table || !row_req || !idx || !out) return DSA_ERR_NULL;
+  if (num_groups > 0 && !groups) return DSA_ERR_NULL;
+  if (rows < 0 || num_groups < 0 || num_groups > rows || num_q_heads < 1 || num_kv_heads < 1 ||
+      k < 1 || max_pages < 1 || !isfinite(scale))
+    return DSA_ERR_SHAPE;
+  if (num_q_heads % num_kv_heads != 0) return DSA_ERR_SHAPE;
+  const int ps = pow2_shift(page_size);
+  if (ps < 0) return DSA_ERR_SHAPE;
+  if (dtype != DSA_BF16 || head_dim != 128 || num_q_heads / num_kv_heads != 8)
+    return DSA_ERR_UNSUPPORTED;
+  if (!aligned(q, 16) || !aligned(k_cache, 16) || !aligned(v_cache, 16) || !aligned(out, 4) ||
+      (out_lse && !aligned(out_lse, 4)) || !aligned(block_table, 4) || !aligned(row_req, 4) ||
+      !aligned(idx, 4) || (groups && !aligned(groups, 4)))
+    return DSA_ERR_ALIGN;
+  if ((long long)num_groups * num_kv_heads > INT32_MAX) return DSA_ERR_SHAPE;
+  if (num_groups == 0) return DSA_OK;
+  return launch_status(dsa::launch_group_attn(q, k_cache, v_cache, block_table, row_req, idx,
+                                              groups, num_groups, num_kv_heads, k, ps, max_pages,
+                                              scale, out, out_lse,
+                                              static_cast<hipStream_t>(stream)));
+}
+
 int dsa_sparse_attn_merged_splits(int rows, int num_q_heads, int num_kv_heads, int head_dim,
                                   int k, dsa_dtype dtype, int* num_splits) {
   if (!num_splits) return DSA_ERR_NULL;

@@ -78,6 +78,15 @@ hipError_t launch_sparse_attn_merged(const void* q, const void* kc, const void* 
                                      int max_pages, float scale, int num_splits, void* out,
                                      float* out_lse, bool bf16, hipStream_t stream);
 
+// Prefill group attention (bf16, head dim 128, 8 query heads per KV head):
+// each group {first_row, n_rows <= 8} of rows of one request attends the
+// union of its rows' ascending selections, row r only its own keys; writes
+// out / out_lse of the groups' rows.
+hipError_t launch_group_attn(const void* q, const void* kc, const void* vc, const int32_t* bt,
+                             const int32_t* row_req, const int32_t* idx, const int32_t* groups,
+                             int num_groups, int hkv, int k, int page_shift, int max_pages,
+                             float scale, void* out, float* out_lse, hipStream_t stream);
+
 // Split count for the merged variant: attn_default_splits rounded down to 1/2/4/8.
 int merged_default_splits(int rows, int hq, int hkv, int d, int k, bool bf16);
 

@@ -57,6 +57,8 @@ _SIGS = {
     "dsa_read_probe": (_I, [_P, _LL, _P, _I, _P]),
     "dsa_sparse_attn": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I, _P]),
     "dsa_merge": (_I, [_P, _P, _I, _I, _I, _I, _P, _P, _I, _P]),
+    "dsa_group_attn": (_I, [_P, _P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _I, _F, _P, _P, _I,
+                            _P]),
     "dsa_sparse_attn_splits": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_I)]),
     "dsa_sparse_attn_merged": (_I, [_P, _P, _P, _P, _P, _P, _I, _I, _I, _I, _I, _I, _I, _F, _I, _P, _P, _I, _P]),
     "dsa_sparse_attn_merged_splits": (_I, [_I, _I, _I, _I, _I, _I, ctypes.POINTER(_I)]),
@@ -368,6 +370,25 @@ def sparse_attn(q, k_cache, v_cache, block_table, row_req, idx, page_size, scale
         _dev(part_o, "part_o", torch.float32), _dev(part_lse, "part_lse", torch.float32), dt],
         stream, prepare)
     return p if prepare else (part_o, part_lse)
+
+
+def group_attn(q, k_cache, v_cache, block_table, row_req, idx, groups, page_size, scale, out,
+               out_lse=None, stream=None, prepare=False):
+    """dsa_group_attn: attention of the rows of each group [first_row, n_rows]
+    over the union of their selections; writes out (and out_lse) in place."""
+    rows, hq, d = q.shape
+    hkv = k_cache.shape[2]
+    dt = _dtype_code(q)
+    if k_cache.dtype != q.dtype or v_cache.dtype != q.dtype or out.dtype != q.dtype:
+        raise TypeError("q, k_cache, v_cache and out dtypes differ")
+    p = _call("dsa_group_attn", [
+        _dev(q, "q"), _dev(k_cache, "k_cache"), _dev(v_cache, "v_cache"),
+        _dev(block_table, "block_table", torch.int32), _dev(row_req, "row_req", torch.int32),
+        _dev(idx, "idx", torch.int32), _dev(groups, "groups", torch.int32), int(groups.shape[0]),
+        rows, hq, hkv, d, int(idx.shape[1]), int(page_size), int(block_table.shape[1]),
+        float(scale), _dev(out, "out"),
+        None if out_lse is None else _dev(out_lse, "out_lse", torch.float32), dt], stream, prepare)
+    return p if prepare else out
 
 
 def sparse_attn_splits(rows, num_q_heads, num_kv_heads, head_dim, k, dtype) -> int:

@@ -16,6 +16,19 @@ import torch
 from . import lib
 
 
+class _Seq:
+    """Prepared library calls issued one after another on one stream."""
+
+    __slots__ = ("calls",)
+
+    def __init__(self, calls):
+        self.calls = calls
+
+    def __call__(self, stream=None):
+        for c in self.calls:
+            c(stream)
+
+
 class DsaStep:
     """Buffers and launches for one step of ``inp`` (a StepInputs on a CUDA
     device). ``block_rows`` > 1 groups consecutive rows of a request into
@@ -32,11 +45,16 @@ class DsaStep:
     indexer count each row's scores by the top bits of their order keys
     (dsa_indexer_scores_hist) and the top-k start from those counts
     (dsa_topk_hist), which leaves them cleared for the next run; it excludes
-    score windows and the two-stage top-k."""
+    score windows and the two-stage top-k. ``group_attn`` runs the attention
+    of the score blocks of several rows (prefill groups, at most 8 rows) over
+    the union of their selections on the matrix cores (dsa_group_attn); rows
+    from the first of the trailing one-row blocks on (decode rows) keep the
+    vector kernel."""
 
     def __init__(self, inp, num_splits: int | None = None, block_rows: int = 1,
                  fused: bool | None = False, topk_chunk: int | None = 0,
-                 score_buffer_bytes: int | None = None, hist: bool = False):
+                 score_buffer_bytes: int | None = None, hist: bool = False,
+                 group_attn: bool = False):
         wl = inp.wl
         dev = inp.q.device
         self.inp = inp
@@ -87,6 +105,19 @@ class DsaStep:
                                     device=dev)
         self.out = torch.empty(self.rows, wl.hq, wl.d, dtype=inp.q.dtype, device=dev)
         self.out_lse = torch.empty(self.rows, wl.hq, dtype=torch.float32, device=dev)
+        # Group attention: the blocks before the trailing one-row blocks.
+        self.group_rows = 0
+        self.groups = None
+        if group_attn:
+            if self.blocks_host is None or block_rows > 8:
+                raise ValueError("group attention needs score blocks of at most 8 rows")
+            nb = len(self.blocks_host)
+            tail = nb
+            while tail > 0 and self.blocks_host[tail - 1][1] == 1:
+                tail -= 1
+            self.group_rows = int(self.blocks_host[tail][0]) if tail < nb else self.rows
+            if tail > 0:
+                self.groups = torch.from_numpy(self.blocks_host[:tail].copy()).to(dev)
         # Zero once; the top-k clears the counts it read.
         self.hist = (torch.zeros(self.rows, lib.HIST_BINS, dtype=torch.int32, device=dev)
                      if hist else None)
@@ -122,7 +153,21 @@ class DsaStep:
             else:
                 self._calls["topk"] = lib.topk(self.scores, self.row_len, wl.topk, self.idx,
                                                total_keys=self.total_keys, prepare=True)
-        if self.fused:
+        if self.groups is not None:
+            calls = [lib.group_attn(i.q, i.k_cache, i.v_cache, i.block_table, self.row_req,
+                                    self.idx, self.groups, wl.page, wl.attn_scale, self.out,
+                                    self.out_lse, prepare=True)]
+            g0 = self.group_rows
+            if g0 < self.rows:
+                # The decode rows after the groups, on the vector kernel.
+                sl = slice(g0, self.rows)
+                splits = lib.sparse_attn_merged_splits(self.rows - g0, wl.hq, wl.hkv, wl.d,
+                                                       wl.topk, i.q.dtype)
+                calls.append(lib.sparse_attn_merged(
+                    i.q[sl], i.k_cache, i.v_cache, i.block_table, self.row_req[sl], self.idx[sl],
+                    wl.page, wl.attn_scale, splits, self.out[sl], self.out_lse[sl], prepare=True))
+            self._calls["attention"] = _Seq(calls)
+        elif self.fused:
             self._calls["attention"] = lib.sparse_attn_merged(
                 i.q, i.k_cache, i.v_cache, i.block_table, self.row_req, self.idx, wl.page,
                 wl.attn_scale, self.num_splits, self.out, self.out_lse, prepare=True)

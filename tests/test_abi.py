@@ -260,6 +260,23 @@ def test_indexer_scores_hist_rejects(kw, code):
     assert lib._lib.dsa_indexer_scores_hist(*a.values()) == code
 
 
+@pytest.mark.parametrize("kw,code", [
+    (dict(q=None), NULL), (dict(groups=None), NULL), (dict(groups=None, num_groups=0), OK),
+    (dict(num_groups=5), SHAPE), (dict(num_q_heads=63), SHAPE), (dict(page_size=48), SHAPE),
+    (dict(head_dim=64), UNSUP), (dict(num_q_heads=32), UNSUP), (dict(dtype=0), UNSUP),
+    (dict(k_cache=A + 8), ALIGN), (dict(rows=0, num_groups=0), OK),
+])
+def test_group_attn_rejects(kw, code):
+    a = dict(q=A, k_cache=A, v_cache=A, block_table=A, row_req=A, idx=A, groups=A, num_groups=2,
+             rows=4, num_q_heads=64, num_kv_heads=8, head_dim=128, k=16, page_size=64,
+             max_pages=4, scale=0.1, out=A, out_lse=None, dtype=1, stream=None)
+    a.update(kw)
+    if kw.get("num_groups", 2) == 0 and code == OK:
+        # accepted and nothing launched
+        pass
+    assert lib._lib.dsa_group_attn(*a.values()) == code
+
+
 def test_topk_chunked_slots():
     assert lib.topk_chunked_slots(4, 128, 16, 32) == 2 * 4 * 4 * 16
     assert lib.topk_chunked_slots(4, 132, 16, 32) == 2 * 4 * 5 * 16

@@ -536,6 +536,89 @@ def test_attention_padding_anywhere(S):
             assert float(np.abs(gl[fl] - wl_[fl]).max()) <= tol_l, r
 
 
+def _prefill_groups_wl(seed=51, topk=256):
+    # Prefill chunks of 37, 9, 8 and 3 rows on short and long prior contexts
+    # (unions spanning several 4096-position windows), plus two decode rows;
+    # 64 query / 8 KV heads of dim 128 (8 heads per group).
+    prior = (700, 5000, 60, 0, 20000, 3000, 9)
+    new = (37, 9, 8, 3, 6, 1, 1)
+    return I.custom(I.decode(), name="prefill_groups", hq=64, hkv=8, topk=topk, prior=prior,
+                    new=new, seed=seed)
+
+
+@pytest.mark.parametrize("block_rows,topk", [(8, 256), (3, 256), (8, 2048), (1, 64)])
+def test_group_attn_matches_oracle(block_rows, topk):
+    """dsa_group_attn (the union of a group's selections with per-row masks,
+    matrix cores) writes every row's attention output and log-sum-exp within
+    the bf16 tolerances of the oracle, for groups of 1..8 rows."""
+    from sparse_attention_decode_02_amd import lib
+    inp = _host_inputs(_prefill_groups_wl(topk=topk))
+    step = run_step(inp, block_rows=1, num_splits=1)
+    groups_host = lib.plan_blocks(step.row_req_host, block_rows)
+    groups = torch.from_numpy(groups_host).cuda()
+    wl = step.wl
+    out = torch.full_like(step.out, float("nan"))
+    lse = torch.full_like(step.out_lse, float("nan"))
+    lib.group_attn(inp.q, inp.k_cache, inp.v_cache, inp.block_table, step.row_req, step.idx,
+                   groups, wl.page, wl.attn_scale, out, lse)
+    torch.cuda.synchronize()
+    _say(f"group attention: {step.rows} rows in {len(groups_host)} groups of <= {block_rows}")
+    worst = 0.0
+    for r in range(step.rows):
+        _, idx, _, _, o, ol = oracle_row(step, r)
+        assert np.array_equal(step.idx[r].cpu().numpy(), idx)
+        go = out[r].double().cpu().numpy()
+        gl = lse[r].double().cpu().numpy()
+        err = float(np.abs(go - o).max())
+        worst = max(worst, err)
+        assert err <= 2e-2, f"row {r}: output error {err}"
+        fin = np.isfinite(ol)
+        assert np.array_equal(np.isfinite(gl), fin), r
+        if fin.any():
+            assert float(np.abs(gl[fin] - ol[fin]).max()) <= 1e-3, f"row {r}: lse"
+    _say(f"  max |out err| {worst:.3g}")
+
+
+def test_group_attn_step():
+    """The step with prefill groups on the matrix cores and the trailing
+    decode rows on the vector kernel: every row against the oracle."""
+    inp = _host_inputs(_prefill_groups_wl(seed=53))
+    step = DsaStep(inp, block_rows=8, fused=None, group_attn=True)
+    step.scores.view(torch.int32).fill_(CANARY)
+    step.run()
+    torch.cuda.synchronize()
+    assert step.groups is not None and step.group_rows < step.rows
+    for r in range(step.rows):
+        _, idx, _, _, o, ol = oracle_row(step, r)
+        assert np.array_equal(step.idx[r].cpu().numpy(), idx)
+        assert float(np.abs(step.out[r].double().cpu().numpy() - o).max()) <= 2e-2, r
+
+
+def test_group_attn_zero_length_rows():
+    """Rows of length 0 inside a group select nothing: output 0, lse -inf,
+    and the group's other rows are unaffected."""
+    from sparse_attention_decode_02_amd import lib
+    inp = _host_inputs(_prefill_groups_wl(seed=52))
+    step = run_step(inp, block_rows=1, num_splits=1)
+    pad = [3, 10, 40]
+    step.row_len[pad] = 0
+    step.run()
+    torch.cuda.synchronize()
+    step.row_len_host = step.row_len.cpu().numpy()
+    groups = torch.from_numpy(lib.plan_blocks(step.row_req_host, 8)).cuda()
+    wl = step.wl
+    out = torch.full_like(step.out, float("nan"))
+    lse = torch.full_like(step.out_lse, float("nan"))
+    lib.group_attn(inp.q, inp.k_cache, inp.v_cache, inp.block_table, step.row_req, step.idx,
+                   groups, wl.page, wl.attn_scale, out, lse)
+    torch.cuda.synchronize()
+    for r in pad:
+        assert bool((out[r].float() == 0).all()) and bool(torch.isneginf(lse[r]).all())
+    for r in (0, 2, 4, 9, 11, 39, 41):
+        _, _, _, _, o, ol = oracle_row(step, r)
+        assert float(np.abs(out[r].double().cpu().numpy() - o).max()) <= 2e-2, r
+
+
 def test_padding_rows_with_zero_length():
     """Rows of length 0 (padding in a fixed-size batch): no score written, all
     slots -1, empty attention (o = 0, lse = -inf), merged output 0."""
@@ -799,6 +882,29 @@ def test_ragged_full_size():
         assert any(1 < x < 2048 for x in L)
         return list(range(s.rows))
     _full(I.ragged(), rows)
+
+
+def test_mixed_group_attn_full_size():
+    """The mixed step with its prefill groups on the matrix cores (union of
+    each 8-row group's selections) and its decode rows on the vector kernel:
+    sampled prefill rows, including each request's first and last, and decode
+    rows against the oracle."""
+    wl = I.mixed()
+    _say(f"{wl.name} with group attention: generating on the device")
+    inp = I.generate(wl, "cuda")
+    step = DsaStep(inp, block_rows=8, fused=None, group_attn=True)
+    step.scores.view(torch.int32).fill_(CANARY)
+    step.run()
+    torch.cuda.synchronize()
+    assert step.group_rows == 2048
+    rows = sorted({0, 7, 8, 63, 511, 512, 1023, 1024, 1535, 1536, 2047, 2048, 2080, 2107})
+    errs = {}
+    for r in rows:
+        e = check_row(step, r)
+        errs = {k: max(errs.get(k, 0.0), v) for k, v in e.items()}
+    _say(f"  {len(rows)} rows ok, max errors {errs}")
+    del step, inp
+    torch.cuda.empty_cache()
 
 
 def test_mixed_full_size():
