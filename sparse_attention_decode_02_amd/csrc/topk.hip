@@ -48,7 +48,9 @@ enum TopkMode {
 };
 
 template <int kThreads, int kVPT, int kMode = kWholeRow>
-__global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict__ scores,
+// 512-thread workgroups keep two per compute unit: four waves per SIMD, so at
+// most 128 registers (the second bound is waves per SIMD, not workgroups).
+__global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel(const float* __restrict__ scores,
                                                        const int32_t* __restrict__ row_len,
                                                        int width, int k,
                                                        int32_t* __restrict__ idx, int seg,
@@ -285,8 +287,20 @@ __global__ __launch_bounds__(kThreads) void topk_kernel(const float* __restrict_
     uint32_t excl_gt, excl_eq, tot_gt, tot_eq;
     // Scans of consecutive chunks use different words; each scan's barrier
     // orders the reads of the one before.
-    block_exclusive_scan2<kTopkWaves>((uint32_t)popcount(gtm), (uint32_t)popcount(eqm),
-                                      emit_sh[c & 1], &excl_gt, &excl_eq, &tot_gt, &tot_eq);
+    if constexpr (kChunk < 65536) {
+      // Both counts of a chunk and their prefix sums stay below 65536, so
+      // they share one word (one scan, fewer registers).
+      uint32_t tot;
+      const uint32_t ex = block_exclusive_scan<kTopkWaves>(
+          ((uint32_t)popcount(gtm) << 16) | (uint32_t)popcount(eqm), emit_sh[c & 1], &tot);
+      excl_gt = ex >> 16;
+      excl_eq = ex & 0xffffu;
+      tot_gt = tot >> 16;
+      tot_eq = tot & 0xffffu;
+    } else {
+      block_exclusive_scan2<kTopkWaves>((uint32_t)popcount(gtm), (uint32_t)popcount(eqm),
+                                        emit_sh[c & 1], &excl_gt, &excl_eq, &tot_gt, &tot_eq);
+    }
     uint32_t g = gt_run + excl_gt;
     uint32_t e = eq_run + excl_eq;
     // The winners' keys (segment mode) are re-read from the row, a cache
