@@ -377,6 +377,9 @@ def main(argv=None):
     ap.add_argument("--hist", type=int, default=0,
                     help="1: the indexer counts each row's scores and the top-k starts from the "
                          "counts (dsa_indexer_scores_hist + dsa_topk_hist)")
+    ap.add_argument("--group-attn", type=int, default=0,
+                    help="1: attention of multi-row score blocks over the union of their "
+                         "selections on the matrix cores (dsa_group_attn)")
     ap.add_argument("--graph", action="store_true",
                     help="record the step into a HIP graph once and time its replays")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
@@ -422,7 +425,7 @@ def main(argv=None):
                 fused=False if args.unfused else None,
                 topk_chunk=None if args.topk_chunk < 0 else args.topk_chunk,
                 score_buffer_bytes=(args.score_buffer_mib << 20) if args.score_buffer_mib else None,
-                hist=bool(args.hist))
+                hist=bool(args.hist), group_attn=bool(args.group_attn))
     step = DsaStep(inp, **opts)
     torch.cuda.synchronize()
     print(f"[bench] rows {step.rows} width {step.width} splits {step.num_splits}",
@@ -485,6 +488,9 @@ def main(argv=None):
                           f"two-stage, {step.topk_chunk}-position segments" if step.topk_chunk
                           else "one pass"),
             "score_rows_per_window": step.window_rows,
+            "attention": ("prefill groups over the union of their selections (matrix cores), "
+                          f"{step.rows - step.group_rows} rows on the vector kernel"
+                          if step.groups is not None else "vector kernel"),
         },
         "hbm_gbps": round(gbps, 1),
         "layer_frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
@@ -514,7 +520,8 @@ def main(argv=None):
     if args.cpu_seconds > 0:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds, torch)
-    names = [n for n in args.configs.split(",") if n and n != args.workload + ("+hist" if args.hist else "")]
+    this = args.workload + ("+hist" if args.hist else "+group" if args.group_attn else "")
+    names = [n for n in args.configs.split(",") if n and n != this]
     if names:
         del step, inp, graph
         torch.cuda.empty_cache()
