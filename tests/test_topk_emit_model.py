@@ -9,11 +9,13 @@ order. This module re-enacts that arithmetic with NumPy for a workgroup of
 shapes the library launches), and compares the slots it produces with the
 oracle's top-k (stable sort, ties to the lower position).
 
-The count scan is modelled at a given field width. The kernel's scan keeps
-both counts at full 32-bit width; an earlier version packed them as two 16-bit
-fields of one word, which loses a carry when all 65536 keys of a chunk tie
-with the threshold. The model shows both: full width matches the oracle on
-every row, the 16-bit packing fails on the fully tied 65536-key chunks.
+The count scan is modelled at a given field width. The kernel packs the two
+counts as 16-bit fields of one word when a chunk holds fewer than 65536 keys
+(no count or prefix sum can reach 65536 there) and scans them at full 32-bit
+width for the 65536-key chunk, where the packing would lose a carry when all
+keys tie with the threshold. The model shows all three: full width and the
+kernel's rule match the oracle on every row at every launched shape, and the
+16-bit packing fails on the fully tied 65536-key chunks.
 """
 
 import numpy as np
@@ -97,6 +99,11 @@ def emit(keys, k, threads, vpt, field_bits=None):
     return out
 
 
+def kernel_field_bits(threads, vpt):
+    """The kernel's choice: one packed word below 65536 keys per chunk."""
+    return 16 if threads * vpt < 65536 else None
+
+
 def _rows():
     rng = np.random.default_rng(3)
     tail = np.concatenate([np.zeros(65536, np.float32), (rng.random(100) + 1).astype(np.float32)])
@@ -120,6 +127,19 @@ def test_full_width_scan_matches_oracle(threads, vpt, k):
     for name, sc in _rows():
         want = O.topk_row(sc, len(sc), k)
         got = emit(order_keys(sc), k, threads, vpt)
+        assert np.array_equal(got, want), (name, np.flatnonzero(got != want)[:5])
+
+
+@pytest.mark.parametrize("threads,vpt", SHAPES)
+@pytest.mark.parametrize("k", [16, 2048])
+def test_kernel_scan_width_matches_oracle(threads, vpt, k):
+    """What the kernel does at each shape: packed counts for the 32768-key
+    and smaller chunks, full width for the 65536-key chunk."""
+    fb = kernel_field_bits(threads, vpt)
+    assert (fb is None) == (threads * vpt == 65536)
+    for name, sc in _rows():
+        want = O.topk_row(sc, len(sc), k)
+        got = emit(order_keys(sc), k, threads, vpt, field_bits=fb)
         assert np.array_equal(got, want), (name, np.flatnonzero(got != want)[:5])
 
 
