@@ -21,7 +21,11 @@
 //     t + 32 the second half (two 128-byte runs per 256-byte bf16 row).
 //   * V: for each token j the whole wave reads its row (lane l gets dims
 //     [l*d/64, (l+1)*d/64)), addressed from token j's row id taken from lane j
-//     as a wave-uniform value, so the address arithmetic is scalar.
+//     as a wave-uniform value, so the address arithmetic is scalar. These
+//     loads carry the nontemporal hint: each instruction reads whole cache
+//     lines that nothing reads again, and with the hint the gather runs ~9%
+//     faster (the K loads, whose instructions touch 16 bytes of 64 lines
+//     each, keep the default: the hint there re-fetches lines).
 //   * scores: each lane dots its half row with the group's G query heads
 //     (LDS broadcasts; v_dot2_f32_bf16 -- exact bf16 products, fp32 sums), and
 //     v_permlane32_swap adds the two halves.
@@ -134,6 +138,18 @@ template <> struct Elem<float, 1> {
   typedef float Word;
   __device__ static float get(Word w, int) { return w; }
 };
+
+// A value-row word loaded as streaming (nontemporal) data: the selected rows
+// are read once, and the hint lets the gathers run closer to the streaming
+// rate.
+template <typename W> __device__ __forceinline__ W load_stream(const W* p) {
+  return __builtin_nontemporal_load(p);
+}
+template <> __device__ __forceinline__ float2 load_stream<float2>(const float2* p) {
+  typedef float f2v __attribute__((ext_vector_type(2)));
+  const f2v v = __builtin_nontemporal_load(reinterpret_cast<const f2v*>(p));
+  return make_float2(v.x, v.y);
+}
 
 // FS == 0: one wave per workgroup and split, partials written to HBM.
 // FS > 0: the FS splits of one (row, KV group) are FS waves of one workgroup
@@ -260,7 +276,7 @@ __global__ __launch_bounds__(64 * (FS > 0 ? FS * PP : 1), (sizeof(T) == 2 && D *
       for (int j = 0; j < kTile; ++j) {
         uint32_t rj = (uint32_t)__builtin_amdgcn_readlane((int)krow, j);
         rj = rj == 0xFFFFFFFFu ? 0u : rj;
-        vw[j] = reinterpret_cast<const Word*>(vgroup + (size_t)rj * kv_stride)[lane];
+        vw[j] = load_stream(reinterpret_cast<const Word*>(vgroup + (size_t)rj * kv_stride) + lane);
       }
       const bool valid = krow != 0xFFFFFFFFu;
       const uint32_t krow_next = tile_row(t + 1);
