@@ -413,8 +413,9 @@ int dsa_sparse_attn_splits(int rows, int num_q_heads, int num_kv_heads, int head
  *   out_lse  device [rows][num_q_heads] float32 (output), or NULL
  *
  * Supported: as dsa_sparse_attn, with num_splits in {1, 2, 4, 6, 8} and
- * num_splits <= k; out 16-byte aligned. (Six splits run two pairs of six
- * waves per workgroup; the result does not depend on it.)
+ * num_splits <= k; out 16-byte aligned. (Six splits of any shape, and eight
+ * splits of bf16 rows with head_dim 128 and eight query heads per KV group,
+ * run two pairs per workgroup; the result does not depend on it.)
  * ------------------------------------------------------------------------ */
 int dsa_sparse_attn_merged(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_table, const int32_t* row_req, const int32_t* idx,

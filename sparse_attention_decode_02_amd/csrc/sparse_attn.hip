@@ -8,7 +8,7 @@
 // One wave per (row, split, KV group); in the merged variant the splits of one
 // (row, KV group) are the waves of one workgroup and are merged through LDS at
 // the end (no partials in HBM, no second launch). The split's slots are walked
-// in tiles of 32 tokens:
+// in tiles of 32 tokens (two lanes per token) or 16 (four lanes per token):
 //   * addresses: a prologue translates up to 512 selected positions through
 //     the block table into cache row ids in LDS (two dependent round trips
 //     per span, not per tile); tiles past the span's last selected slot are
@@ -18,7 +18,8 @@
 //     reads cache row 0 with probability 0), so each wait covers exactly the
 //     data in use.
 //   * K: lane t reads the first half of token t's row for the group, lane
-//     t + 32 the second half (two 128-byte runs per 256-byte bf16 row).
+//     t + 32 the second half (two 128-byte runs per 256-byte bf16 row); with
+//     16-token tiles lanes t, t+16, t+32, t+48 read its quarters.
 //   * V: for each token j the whole wave reads its row (lane l gets dims
 //     [l*d/64, (l+1)*d/64)), addressed from token j's row id taken from lane j
 //     as a wave-uniform value, so the address arithmetic is scalar. These
@@ -26,9 +27,9 @@
 //     lines that nothing reads again, and with the hint the gather runs ~9%
 //     faster (the K loads, whose instructions touch 16 bytes of 64 lines
 //     each, keep the default: the hint there re-fetches lines).
-//   * scores: each lane dots its half row with the group's G query heads
+//   * scores: each lane dots its part of the row with the group's G query heads
 //     (LDS broadcasts; v_dot2_f32_bf16 -- exact bf16 products, fp32 sums), and
-//     v_permlane32_swap adds the two halves.
+//     row swaps (v_permlane16_swap, v_permlane32_swap) add the parts.
 //   * online softmax in base 2 (the scale folds in log2 e) against a deferred
 //     reference that is raised (one DPP wave max per head, and a rescale)
 //     only when a score overtakes it by more than 2^8; the running sum stays
@@ -46,7 +47,6 @@ typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
-constexpr int kTile = 32;   // tokens per tile
 constexpr int kSpan = 512;  // slots whose cache rows are resolved at once
 constexpr float kSlack = 8.0f;  // log2 headroom of the deferred softmax reference
 
@@ -106,8 +106,15 @@ __device__ __forceinline__ int wave_max_i32(int v) {
   return v;
 }
 
-// x[lane] + x[lane ^ 32]
-__device__ __forceinline__ float add_halves(float x) {
+// x summed over the LPT lanes of a token: x[lane] + x[lane ^ 32] (LPT 2), or
+// over the four 16-lane rows (LPT 4); every such lane gets the sum.
+template <int LPT>
+__device__ __forceinline__ float sum_token_lanes(float x) {
+  if constexpr (LPT == 4) {
+    const auto pr = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                     false);
+    x = __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
+  }
   const auto pr = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
                                                    false);
   return __uint_as_float(pr[0]) + __uint_as_float(pr[1]);
@@ -156,8 +163,12 @@ template <> __device__ __forceinline__ float2 load_stream<float2>(const float2* 
 // and are merged through LDS into the final output (see the end); a
 // workgroup holds PP such pairs (PP * FS waves), so that its waves can fill
 // a CU's wave slots exactly (a workgroup's waves are all placed on one CU).
-template <typename T, int D, int G, int FS, int PP = 1>
-__global__ __launch_bounds__(64 * (FS > 0 ? FS * PP : 1), (sizeof(T) == 2 && D * G <= 1024) ? 3 : 2) void sparse_attn_kernel(
+// LPT lanes share a token: 2 (32-token tiles, each lane a half row) or 4
+// (16-token tiles, quarter rows: fewer registers in flight per wave, so four
+// waves fit a SIMD).
+template <typename T, int D, int G, int FS, int PP = 1, int LPT = 2>
+__global__ __launch_bounds__(64 * (FS > 0 ? FS * PP : 1),
+                             LPT == 4 ? 4 : (sizeof(T) == 2 && D * G <= 1024) ? 3 : 2) void sparse_attn_kernel(
     const T* __restrict__ q, const T* __restrict__ kc, const T* __restrict__ vc,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ row_req,
     const int32_t* __restrict__ idx, int hkv, int k, int page_shift, int max_pages,
@@ -166,20 +177,21 @@ __global__ __launch_bounds__(64 * (FS > 0 ? FS * PP : 1), (sizeof(T) == 2 && D *
     int npairs) {
   constexpr bool kBf16 = sizeof(T) == 2;
   constexpr int RW = D * (int)sizeof(T) / 4;  // 32-bit words per row
-  constexpr int NV4 = RW / 8;                 // uint4 per half row
+  constexpr int TT = 64 / LPT;                // tokens per tile
+  constexpr int NV4 = RW / 4 / LPT;           // uint4 per lane's part of a row
   constexpr int DPL = D / 64;                 // output dims per lane
   constexpr int NW = FS > 0 ? FS * PP : 1;    // waves per workgroup
   typedef Elem<T, DPL> E;
   typedef typename E::Word Word;
   __shared__ uint4 q_lds_all[PP][G * RW / 4];
-  __shared__ float p_lds_all[NW][kTile * G];
+  __shared__ float p_lds_all[NW][TT * G];
   __shared__ uint32_t rows_lds_all[NW][kSpan];
 
   const int lane = threadIdx.x & 63;
   // Uniform across the wave: everything derived from it (the pair, the
   // split, LDS slots, cache and index pointers) stays in scalar registers.
   const int wave = __builtin_amdgcn_readfirstlane((int)(threadIdx.x >> 6));
-  const int tl = lane & 31, hf = lane >> 5;
+  const int tl = lane % TT, hf = lane / TT;  // token of the tile, part of its row
   // (row, KV group) pair of this wave; a workgroup's last pairs may not exist
   // (their waves skip the work but still meet the workgroup barriers).
   const int pw = FS > 0 ? wave / FS : 0;  // pair within the workgroup
@@ -250,11 +262,11 @@ __global__ __launch_bounds__(64 * (FS > 0 ? FS * PP : 1), (sizeof(T) == 2 && D *
     }
     last = __builtin_amdgcn_readfirstlane(wave_max_i32(last));  // uniform: a scalar loop bound
     wave_sync();
-    const int ntiles = (last + kTile) / kTile;  // tiles up to the last selected slot
+    const int ntiles = (last + TT) / TT;  // tiles up to the last selected slot
 
-    // Row ids of tile t for this lane's token (lanes t and t+32 share one).
+    // Row ids of tile t for this lane's token (shared by its LPT lanes).
     auto tile_row = [&](int t) -> uint32_t {
-      const int i = t * kTile + tl;
+      const int i = t * TT + tl;
       return i < n ? rows_lds[i] : 0xFFFFFFFFu;
     };
     // Loads are unconditional: a padding slot reads cache row 0 and gets
@@ -271,9 +283,9 @@ __global__ __launch_bounds__(64 * (FS > 0 ? FS * PP : 1), (sizeof(T) == 2 && D *
     load_k(krow, kv);
     for (int t = 0; t < ntiles; ++t) {
       // V of tile t: one whole row per token, its row id wave-uniform.
-      Word vw[kTile];
+      Word vw[TT];
 #pragma unroll
-      for (int j = 0; j < kTile; ++j) {
+      for (int j = 0; j < TT; ++j) {
         uint32_t rj = (uint32_t)__builtin_amdgcn_readlane((int)krow, j);
         rj = rj == 0xFFFFFFFFu ? 0u : rj;
         vw[j] = load_stream(reinterpret_cast<const Word*>(vgroup + (size_t)rj * kv_stride) + lane);
@@ -302,7 +314,7 @@ __global__ __launch_bounds__(64 * (FS > 0 ? FS * PP : 1), (sizeof(T) == 2 && D *
             acc = fmaf(__uint_as_float(kv[c].w), __uint_as_float(qv.w), acc);
           }
         }
-        sc[h] = valid ? add_halves(acc) * scale_log2 : -INFINITY;
+        sc[h] = valid ? sum_token_lanes<LPT>(acc) * scale_log2 : -INFINITY;
       }
       // K of tile t+1 in flight while tile t's values are summed.
       load_k(krow_next, kv);
@@ -338,7 +350,7 @@ __global__ __launch_bounds__(64 * (FS > 0 ? FS * PP : 1), (sizeof(T) == 2 && D *
       wave_sync();
 
 #pragma unroll
-      for (int j = 0; j < kTile; ++j) {
+      for (int j = 0; j < TT; ++j) {
         float pj[G];
 #pragma unroll
         for (int h = 0; h < G; ++h) pj[h] = p_lds[j * G + h];
@@ -410,6 +422,23 @@ __global__ __launch_bounds__(64 * (FS > 0 ? FS * PP : 1), (sizeof(T) == 2 && D *
   }
 }
 
+// Lanes per token. bf16 rows with d = 128 and eight query heads per KV group
+// (the decode shape of the method's models) can take 16-token tiles: 120
+// registers, so four waves share a SIMD where 32-token tiles (168) allow
+// three. That hides load latency in batches of up to a few waves per SIMD
+// (~6% faster at batch 64); past that the kernel is bound by its vector
+// arithmetic, which 32-token tiles spend less of per token. The choice
+// depends only on the shape and rows x KV groups, so the merged and
+// two-launch paths of one call shape use the same tiles and stay bitwise
+// equal.
+template <typename T, int D, int G>
+constexpr bool quarter_tiles_shape() {
+  return sizeof(T) == 2 && D == 128 && G == 8;
+}
+static bool quarter_tiles(bool shape_ok, long long pairs) {
+  return shape_ok && pairs <= 8LL * device_cus();
+}
+
 template <typename T, int FS, int PP = 1>
 static hipError_t launch_attn_t(const T* q, const T* kc, const T* vc, const int32_t* bt,
                                 const int32_t* row_req, const int32_t* idx, int rows, int hq,
@@ -422,10 +451,17 @@ static hipError_t launch_attn_t(const T* q, const T* kc, const T* vc, const int3
   const dim3 grid(FS > 0 ? (unsigned)((npairs + PP - 1) / PP) : (unsigned)rows * S * hkv);
   const dim3 block(64 * (FS > 0 ? FS * PP : 1));
   const float sl2 = scale * kLog2e;
-#define DSA_ATTN(D_, G_)                                                                        \
-  hipLaunchKernelGGL((sparse_attn_kernel<T, D_, G_, FS, PP>), grid, block, 0, stream, q, kc, vc, \
-                     bt, row_req, idx, hkv, k, page_shift, max_pages, sl2, S, chunk, part_o,      \
+#define DSA_ATTN_L(D_, G_, L_)                                                                  \
+  hipLaunchKernelGGL((sparse_attn_kernel<T, D_, G_, FS, PP, L_>), grid, block, 0, stream, q, kc,  \
+                     vc, bt, row_req, idx, hkv, k, page_shift, max_pages, sl2, S, chunk, part_o,  \
                      part_lse, out, out_lse, npairs)
+#define DSA_ATTN(D_, G_)                                                       \
+  if constexpr (quarter_tiles_shape<T, D_, G_>()) {                            \
+    if (quarter_tiles(true, npairs)) DSA_ATTN_L(D_, G_, 4);                    \
+    else DSA_ATTN_L(D_, G_, 2);                                                \
+  } else {                                                                     \
+    DSA_ATTN_L(D_, G_, 2);                                                     \
+  }
 #define DSA_ATTN_G(D_)                    \
   switch (G) {                            \
     case 1: DSA_ATTN(D_, 1); break;       \
@@ -444,13 +480,18 @@ static hipError_t launch_attn_t(const T* q, const T* kc, const T* vc, const int3
   }
 #undef DSA_ATTN_G
 #undef DSA_ATTN
+#undef DSA_ATTN_L
   return hipGetLastError();
 }
 
 template <typename T>
-static const void* attn_kernel_ptr(int d, int G) {
-#define DSA_ATTN_PTR(D_, G_) \
-  if (d == D_ && G == G_) return (const void*)sparse_attn_kernel<T, D_, G_, 0>;
+static const void* attn_kernel_ptr(int d, int G, long long pairs) {
+#define DSA_ATTN_PTR(D_, G_)                                                               \
+  if (d == D_ && G == G_) {                                                                \
+    if (quarter_tiles(quarter_tiles_shape<T, D_, G_>(), pairs))                              \
+      return (const void*)sparse_attn_kernel<T, D_, G_, 0, 1, quarter_tiles_shape<T, D_, G_>() ? 4 : 2>; \
+    return (const void*)sparse_attn_kernel<T, D_, G_, 0, 1, 2>;                           \
+  }
   DSA_ATTN_PTR(128, 1) DSA_ATTN_PTR(128, 2) DSA_ATTN_PTR(128, 4) DSA_ATTN_PTR(128, 8)
   DSA_ATTN_PTR(128, 16) DSA_ATTN_PTR(64, 1) DSA_ATTN_PTR(64, 2) DSA_ATTN_PTR(64, 4)
   DSA_ATTN_PTR(64, 8) DSA_ATTN_PTR(64, 16)
@@ -459,13 +500,15 @@ static const void* attn_kernel_ptr(int d, int G) {
 }
 
 int attn_default_splits(int rows, int hq, int hkv, int d, int k, bool bf16) {
-  const void* kern = bf16 ? attn_kernel_ptr<uint16_t>(d, hq / hkv) : attn_kernel_ptr<float>(d, hq / hkv);
+  const long long pairs = (long long)rows * hkv;
+  const void* kern = bf16 ? attn_kernel_ptr<uint16_t>(d, hq / hkv, pairs)
+                          : attn_kernel_ptr<float>(d, hq / hkv, pairs);
   int cap = kern ? device_capacity(kern, 64) : 0;
   if (cap <= 0) cap = 3072;
   // Waves of one launch ~ two thirds of the device's capacity: longer waves
   // amortize their prologue (query load, position -> row resolution) better
   // than a full first round does; each split keeps >= 32 slots.
-  const long long waves = (long long)rows * hkv;
+  const long long waves = pairs;
   const long long target = 2LL * cap / 3;
   int s = (int)((target + waves / 2) / waves);
   const int max_s = max(1, k / 32);
@@ -486,6 +529,22 @@ hipError_t launch_sparse_attn(const void* q, const void* kc, const void* vc, con
                                  static_cast<const float*>(vc), bt, row_req, idx, rows, hq, hkv, d,
                                  k, page_shift, max_pages, scale, num_splits, part_o, part_lse,
                                  nullptr, nullptr, stream);
+}
+
+// Eight splits of the 16-token-tile shape: two (row, KV group) pairs per
+// 16-wave workgroup fill a CU at four waves per SIMD.
+static hipError_t launch_merged_q4(const uint16_t* q, const uint16_t* kc, const uint16_t* vc,
+                                   const int32_t* bt, const int32_t* row_req, const int32_t* idx,
+                                   int rows, int hkv, int k, int page_shift, int max_pages,
+                                   float scale, void* out, float* out_lse, hipStream_t stream) {
+  constexpr int kS = 8, kPP = 2;
+  const int npairs = rows * hkv;
+  const int chunk = (k + kS - 1) / kS;
+  hipLaunchKernelGGL((sparse_attn_kernel<uint16_t, 128, 8, kS, kPP, 4>),
+                     dim3((unsigned)((npairs + kPP - 1) / kPP)), dim3(64 * kS * kPP), 0, stream, q,
+                     kc, vc, bt, row_req, idx, hkv, k, page_shift, max_pages, scale * kLog2e, kS,
+                     chunk, nullptr, nullptr, out, out_lse, npairs);
+  return hipGetLastError();
 }
 
 template <typename T>
@@ -510,7 +569,14 @@ static hipError_t launch_merged_t(const void* q, const void* kc, const void* vc,
     case 2: DSA_MERGED(2, 1);
     case 4: DSA_MERGED(4, 1);
     case 6: DSA_MERGED(6, kPairs6);
-    case 8: DSA_MERGED(8, 1);
+    case 8:
+      // With 16-token tiles two pairs (16 waves) fit a workgroup.
+      if (quarter_tiles(sizeof(T) == 2 && d == 128 && hq == 8 * hkv, (long long)rows * hkv))
+        return launch_merged_q4(reinterpret_cast<const uint16_t*>(q_),
+                                reinterpret_cast<const uint16_t*>(k_),
+                                reinterpret_cast<const uint16_t*>(v_), bt, row_req, idx, rows, hkv,
+                                k, page_shift, max_pages, scale, out, out_lse, stream);
+      DSA_MERGED(8, 1);
     default: return hipErrorInvalidValue;
   }
 #undef DSA_MERGED
@@ -529,18 +595,25 @@ hipError_t launch_sparse_attn_merged(const void* q, const void* kc, const void* 
 }
 
 int merged_default_splits(int rows, int hq, int hkv, int d, int k, bool bf16) {
-  // Six splits in workgroups of two pairs when that fills the device in one
-  // round at three waves per SIMD (the rows x KV groups are many, the
-  // occupancy allows it); otherwise the split kernel's suggestion rounded
-  // down to a supported workgroup size (1, 2, 4 or 8 waves).
-  const void* kern = bf16 ? attn_kernel_ptr<uint16_t>(d, hq / hkv) : attn_kernel_ptr<float>(d, hq / hkv);
+  // Eight splits (16-token tiles) or six (32-token tiles) in workgroups of
+  // two pairs when that fills the device in about one round at four or three
+  // waves per SIMD (the rows x KV groups are many, the occupancy allows it);
+  // otherwise the split kernel's suggestion rounded down to a supported
+  // workgroup size (1, 2, 4 or 8 waves).
+  const long long pairs = (long long)rows * hkv;
+  const void* kern = bf16 ? attn_kernel_ptr<uint16_t>(d, hq / hkv, pairs)
+                          : attn_kernel_ptr<float>(d, hq / hkv, pairs);
   int cus = device_cus();
   int cap = kern ? device_capacity(kern, 64) : 0;
   if (cap <= 0 || cus <= 0) {
     cus = 256;
     cap = 3072;
   }
-  const long long pairs = (long long)rows * hkv;
+  // The 16-token-tile shape: eight splits, two pairs per 16-wave workgroup,
+  // when the batch fills between half the device's wave slots and two rounds.
+  if (bf16 && d == 128 && hq == 8 * hkv && cap / cus == 16 && k >= 8 * 16 && pairs * 8 * 2 >= cap &&
+      pairs * 8 <= 2LL * cap)
+    return 8;
   if (cap / cus == 12 && k >= 6 * 32 && pairs * 6 <= cap && pairs * 6 * 2 >= cap) return 6;
   const int s = attn_default_splits(rows, hq, hkv, d, k, bf16);
   int f = 1;

@@ -34,9 +34,9 @@ class DsaStep:
     device). ``block_rows`` > 1 groups consecutive rows of a request into
     score blocks for the indexer. ``fused`` runs attention and the merge as
     one launch (dsa_sparse_attn_merged) instead of two; None picks the fused
-    launch whenever its workgroup of splits can hold the split count the
-    library suggests (<= 8 splits, a power of two), and the two launches for
-    small batches that want many splits. ``topk_chunk`` > 0 selects in two
+    launch (with the library's merged split count) unless the batch is small
+    enough that the two-launch kernel wants more than 8 splits, and for a
+    given ``num_splits`` whenever the merged launch supports it. ``topk_chunk`` > 0 selects in two
     stages over segments of that many positions (dsa_topk_chunked), None
     takes the library's suggestion for the sizes, 0 the one-pass kernel.
     ``score_buffer_bytes`` bounds the score memory: rows are scored and
@@ -72,8 +72,10 @@ class DsaStep:
             self.blocks = torch.from_numpy(self.blocks_host).to(dev)
         shape = (self.rows, wl.hq, wl.hkv, wl.d, wl.topk, inp.q.dtype)
         if fused is None:
-            s = num_splits or lib.sparse_attn_splits(*shape)
-            fused = s <= 8 and (s & (s - 1)) == 0
+            if num_splits:
+                fused = num_splits in (1, 2, 4, 6, 8)
+            else:
+                fused = lib.sparse_attn_splits(*shape) <= 8
         self.fused = fused
         splits_of = lib.sparse_attn_merged_splits if fused else lib.sparse_attn_splits
         self.num_splits = num_splits or splits_of(*shape)
