@@ -53,6 +53,20 @@ __device__ __forceinline__ void wave_max_min(uint32_t& mx, uint32_t& mn) {
   mn = min(min(lane_u32(mn, 0), lane_u32(mn, 16)), min(lane_u32(mn, 32), lane_u32(mn, 48)));
 }
 
+// Bitwise OR and AND over the wave, wave-uniform (the same butterflies).
+__device__ __forceinline__ void wave_or_and(uint32_t& o, uint32_t& a) {
+  o |= dpp_u32<0xB1>(o);
+  a &= dpp_u32<0xB1>(a);
+  o |= dpp_u32<0x4E>(o);
+  a &= dpp_u32<0x4E>(a);
+  o |= dpp_u32<0x141>(o);
+  a &= dpp_u32<0x141>(a);
+  o |= dpp_u32<0x140>(o);
+  a &= dpp_u32<0x140>(a);
+  o = lane_u32(o, 0) | lane_u32(o, 16) | lane_u32(o, 32) | lane_u32(o, 48);
+  a = lane_u32(a, 0) & lane_u32(a, 16) & lane_u32(a, 32) & lane_u32(a, 48);
+}
+
 // Inclusive prefix sum over the wave in lane order: shifts by 1, 2, 4, 8
 // inside each 16-lane row (lanes shifted in from outside the row read 0),
 // then the totals of the rows below.

@@ -64,7 +64,7 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
   __shared__ uint32_t hist[2][kBins];  // alternate passes: one fills while the other is cleared
   __shared__ uint32_t scan_sh[2][kTopkWaves];      // per-wave words of the radix passes' scans
   __shared__ uint32_t emit_sh[2][2 * kTopkWaves];  // ... and of the emit's, by chunk parity
-  __shared__ uint32_t red[2 * kTopkWaves];
+  __shared__ uint32_t red[4 * kTopkWaves];
   __shared__ uint32_t pick[3];
 
   const int tid = threadIdx.x;
@@ -146,8 +146,8 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
   if (resident) load_chunk(0);
   for (int i = tid; i < kBins; i += kTopkThreads) hist[0][i] = 0u;  // while the keys arrive
 
-  // ---- min / max over the row --------------------------------------------
-  uint32_t mx = 0u, mn = 0xFFFFFFFFu;
+  // ---- min / max over the row, and the bits every key shares ----------------
+  uint32_t mx = 0u, mn = 0xFFFFFFFFu, oa = 0u, aa = 0xFFFFFFFFu;
   for (int c = 0; c < nchunks; ++c) {
     if (!resident) load_chunk(c);
     if (nv == kVPT) {
@@ -155,6 +155,8 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
       for (int j = 0; j < kVPT; ++j) {
         mx = max(mx, key[j]);
         mn = min(mn, key[j]);
+        oa |= key[j];
+        aa &= key[j];
       }
     } else {
 #pragma unroll
@@ -162,21 +164,30 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
         if (j < nv) {
           mx = max(mx, key[j]);
           mn = min(mn, key[j]);
+          oa |= key[j];
+          aa &= key[j];
         }
     }
   }
   wave_max_min(mx, mn);
+  wave_or_and(oa, aa);
   if (lane == 0) {
     red[wave] = mx;
     red[kTopkWaves + wave] = mn;
+    red[2 * kTopkWaves + wave] = oa;
+    red[3 * kTopkWaves + wave] = aa;
   }
   __syncthreads();
   mx = 0u;
   mn = 0xFFFFFFFFu;
+  oa = 0u;
+  aa = 0xFFFFFFFFu;
 #pragma unroll
   for (int i = 0; i < kTopkWaves; ++i) {
     mx = max(mx, red[i]);
     mn = min(mn, red[kTopkWaves + i]);
+    oa |= red[2 * kTopkWaves + i];
+    aa &= red[3 * kTopkWaves + i];
   }
 
   // ---- radix select of the threshold prefix --------------------------------
@@ -185,7 +196,10 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
   // taken. Every key shares the bits above the highest bit where the row's
   // min and max differ, so the first digit starts there and needs no prefix
   // test.
-  int shift;
+  // Bits below the lowest one where any two keys differ are the same in every
+  // key (the trailing zeros of short dyadic significands, say), so the
+  // passes stop there: comparing the bits above it compares whole keys.
+  int shift, low = 0;
   uint32_t prefix;
   uint32_t need = (uint32_t)k;
   if (mx == mn) {
@@ -194,14 +208,15 @@ __global__ __launch_bounds__(kThreads, kThreads == 512 ? 4 : 1) void topk_kernel
   } else {
     shift = 32 - __clz(mx ^ mn);
     prefix = high_bits(mx, shift);
+    low = __ffs(oa ^ aa) - 1;
   }
   // Three barriers per pass: after the histogram, inside the bin scan, and
   // after the pick. The next pass's histogram buffer is cleared while this
   // one is read, and every scan has its own per-wave words.
   bool first = true;
   int hb = 0;
-  while (shift > 0) {
-    const int nb = min(kDigitBits, shift);
+  while (shift > low) {
+    const int nb = min(kDigitBits, shift - low);
     const int ns = shift - nb;
     const int nbins = 1 << nb;
     const uint32_t dmask = (uint32_t)nbins - 1u;

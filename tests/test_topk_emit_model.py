@@ -40,10 +40,13 @@ def radix_threshold(keys, k):
         return 0, mx, k
     shift = (mx ^ mn).bit_length()
     prefix = mx >> shift if shift < 32 else 0
+    # bits below the lowest one where two keys differ are shared by all keys
+    varying = int(np.bitwise_or.reduce(keys)) ^ int(np.bitwise_and.reduce(keys))
+    low = (varying & -varying).bit_length() - 1
     need = k
     first = True
-    while shift > 0:
-        nb = min(12, shift)
+    while shift > low:
+        nb = min(12, shift - low)
         ns = shift - nb
         cand = keys if first else keys[(keys >> shift) == prefix]
         hist = np.bincount((cand >> ns) & ((1 << nb) - 1), minlength=1 << nb)
@@ -155,6 +158,19 @@ def test_packed_16bit_counts_fail_on_tied_full_chunk(k):
             bad.append(name)
     assert set(bad) == {"70000 equal", "70000 zeros", "65536 zeros then positives"} - (
         {"65536 zeros then positives"} if k <= 100 else set())
+
+
+def test_radix_passes_skip_shared_low_bits():
+    """Dyadic scores with short significands share their low key bits: the
+    passes stop above them and still find the k-th key."""
+    rng = np.random.default_rng(5)
+    sc = (np.round(rng.normal(2240, 400, 32768) * 2) / 2).astype(np.float32)
+    keys = order_keys(sc)
+    shift, prefix, need = radix_threshold(keys, 2048)
+    assert shift >= 11
+    kth = np.sort(keys)[::-1][2047]
+    assert (kth >> shift) == prefix
+    assert np.array_equal(emit(keys, 2048, 1024, 32), O.topk_row(sc, len(sc), 2048))
 
 
 def test_radix_threshold_is_the_kth_key():
