@@ -50,6 +50,7 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __rest
   __shared__ uint32_t scan_sh[3][kWaves];       // per-wave words: passes (2), histogram row (1)
   __shared__ uint32_t emit_sh[2][2 * kWaves];   // per-wave words of the compaction / emit scans
   __shared__ uint32_t pick[3];
+  __shared__ uint32_t red[2 * kWaves];          // per-wave OR / AND of the list's candidates
   __shared__ uint32_t lkey[kCap];               // the list: keys at or above the prefix ...
   __shared__ int32_t lpos[kCap];                // ... and their positions, in position order
 
@@ -142,8 +143,9 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __rest
   // One radix pass: the next <= 12 bits of the keys tied with the prefix.
   // `count` adds this thread's candidates to the histogram h.
   int hb = 0;
+  int low = 0;  // the passes stop at this bit (see step 4)
   auto radix_pass = [&](auto&& count) {
-    const int nb = min(kDigitBits, shift);
+    const int nb = min(kDigitBits, shift - low);
     const int ns = shift - nb;
     const int nbins = 1 << nb;
     uint32_t* h = hbuf[hb];
@@ -260,7 +262,35 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __rest
     uint32_t lk[kEPT];
 #pragma unroll
     for (int j = 0; j < kEPT; ++j) lk[j] = j < ne ? lkey[e0 + j] : 0u;
-    while (!done && shift > 0) {
+    if (!done) {
+      // Bits below the lowest one where two candidates differ are shared by
+      // all of them (the trailing zeros of short dyadic significands, say):
+      // the passes stop there, where equal prefixes mean equal keys.
+      uint32_t oa = 0u, aa = 0xFFFFFFFFu;
+#pragma unroll
+      for (int j = 0; j < kEPT; ++j)
+        if (j < ne && high_bits(lk[j], shift) == prefix) {
+          oa |= lk[j];
+          aa &= lk[j];
+        }
+      wave_or_and(oa, aa);
+      const int lane = tid & 63, wave = tid >> 6;
+      if (lane == 0) {
+        red[wave] = oa;
+        red[kWaves + wave] = aa;
+      }
+      __syncthreads();
+      oa = 0u;
+      aa = 0xFFFFFFFFu;
+#pragma unroll
+      for (int i = 0; i < kWaves; ++i) {
+        oa |= red[i];
+        aa &= red[kWaves + i];
+      }
+      // All candidates equal: no pass is left, the ties go by position.
+      low = (oa ^ aa) ? min(shift, __ffs(oa ^ aa) - 1) : shift;
+    }
+    while (!done && shift > low) {
       radix_pass([&](uint32_t* h, int ns, uint32_t dmask) {
 #pragma unroll
         for (int j = 0; j < kEPT; ++j)
