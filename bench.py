@@ -133,7 +133,7 @@ def _pct(v, q):
     return v[min(len(v) - 1, int(round(q * (len(v) - 1))))]
 
 
-def read_floor_gbps(torch, mib=1024, reps=50):
+def read_floor_gbps(torch, mib=1024, reps=200):
     """A plain streaming read of ``mib`` MiB (dsa_read_probe): the practical
     read bandwidth the layer's GB/s is compared with."""
     from sparse_attention_decode_02_amd import lib
@@ -432,18 +432,26 @@ def main(argv=None):
           file=sys.stderr, flush=True)
 
     graph = step.capture() if args.graph else None
-    # The read floor is measured first, over ~8 ms of streaming reads: this
-    # also brings the GPU to its working clocks, which it otherwise reaches
-    # only ~10 ms into a run (steps timed right after a short warm-up measure
-    # ~5% slower than the same steps later in the run).
-    floor = read_floor_gbps(torch)
-    trace = []
-    ms = time_steps(step, args.steps, args.warmup, torch, graph, trace)
-    kern = time_kernels(step, args.steps, torch)
+    # The read floor is measured first, over ~33 ms of streaming reads: this
+    # also brings the GPU toward its working clocks, which it otherwise
+    # reaches only ~15 ms into a run (steps timed right after a short warm-up
+    # measure up to ~5% slower than the same steps later in the run).
+    floor = read_floor_gbps(torch, reps=200)
+    # The per-kernel and single-step measurements come next; they also run
+    # the step's kernels long enough for the clocks to settle (after the
+    # floor alone the first few dozen steps still run up to ~5% slower), so
+    # the timed steps measure the sustained rate.
     warm = time_per_step(step, args.steps, torch)
     scrub = torch.empty(1 << 28, dtype=torch.float32, device="cuda")  # 1 GiB > L2 + MALL
     cold = time_per_step(step, args.steps, torch, scrub)
     del scrub
+    kern = time_kernels(step, args.steps, torch)
+    # The timed steps carry no events between them: each timing event is a
+    # barrier with a cache write-back on the stream, ~3 us per step at the
+    # headline. Each step's own time comes from a second pass afterwards.
+    ms = time_steps(step, args.steps, args.warmup, torch, graph)
+    trace = []
+    time_steps(step, args.steps, 0, torch, graph, trace)
     layer_us = ms * 1000.0
     ab = algorithmic_bytes(wl, step.row_len_host)
     total_bytes = sum(ab.values())
@@ -501,7 +509,7 @@ def main(argv=None):
                      "p90": round(_pct(cold, 0.9), 2),
                      "note": "a 1 GiB buffer is read before each step, outside its events"},
         },
-        "timed_steps_us": trace,
+        "timed_steps_us": trace,  # a second pass of as many steps, events between them
         "read_floor_gbps": round(floor, 1),
         "layer_frac_of_read_floor": round(gbps / floor, 4),
         "algorithmic_bytes": total_bytes,
