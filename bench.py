@@ -283,10 +283,12 @@ def measure_configs(names, steps, warmup, torch):
     for spec in names:
         name, _, opt = spec.partition("+")
         hist = opt == "hist"
-        group = opt == "group"
+        # the step's automatic choice, or group attention forced on / off
+        group = True if opt == "group" else False if opt == "vector" else None
         wl = I.WORKLOADS[name]()
         print(f"[bench] config {wl.name}{' (histogram top-k)' if hist else ''}"
-              f"{' (group attention)' if group else ''}", file=sys.stderr, flush=True)
+              f"{' (group attention)' if group else ' (vector attention)' if group is False else ''}",
+              file=sys.stderr, flush=True)
         inp = I.generate(wl, "cuda")
         step = DsaStep(inp, block_rows=8, fused=None, topk_chunk=0 if hist else None, hist=hist,
                        group_attn=group)
@@ -377,15 +379,16 @@ def main(argv=None):
     ap.add_argument("--hist", type=int, default=0,
                     help="1: the indexer counts each row's scores and the top-k starts from the "
                          "counts (dsa_indexer_scores_hist + dsa_topk_hist)")
-    ap.add_argument("--group-attn", type=int, default=0,
+    ap.add_argument("--group-attn", type=int, default=-1,
                     help="1: attention of multi-row score blocks over the union of their "
-                         "selections on the matrix cores (dsa_group_attn)")
+                         "selections on the matrix cores (dsa_group_attn); 0: every row on the "
+                         "vector kernel; -1 (default): the step's automatic choice")
     ap.add_argument("--graph", action="store_true",
                     help="record the step into a HIP graph once and time its replays")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="oracle time budget for cpu_baseline, per core setting (0 = skip)")
     ap.add_argument("--configs",
-                    default="tiny,decode,ragged,mixed,ragged+hist,mixed+group,long,long+hist",
+                    default="tiny,decode,ragged,mixed,ragged+hist,mixed+vector,long,long+hist",
                     help="other workloads measured in the same run (comma list, '' = none; "
                          "name+hist: with the histogram top-k)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
@@ -425,7 +428,8 @@ def main(argv=None):
                 fused=False if args.unfused else None,
                 topk_chunk=None if args.topk_chunk < 0 else args.topk_chunk,
                 score_buffer_bytes=(args.score_buffer_mib << 20) if args.score_buffer_mib else None,
-                hist=bool(args.hist), group_attn=bool(args.group_attn))
+                hist=bool(args.hist),
+                group_attn=None if args.group_attn < 0 else bool(args.group_attn))
     step = DsaStep(inp, **opts)
     torch.cuda.synchronize()
     print(f"[bench] rows {step.rows} width {step.width} splits {step.num_splits}",
@@ -528,7 +532,8 @@ def main(argv=None):
     if args.cpu_seconds > 0:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds, torch)
-    this = args.workload + ("+hist" if args.hist else "+group" if args.group_attn else "")
+    this = args.workload + ("+hist" if args.hist else "+group" if args.group_attn > 0
+                            else "+vector" if args.group_attn == 0 else "")
     names = [n for n in args.configs.split(",") if n and n != this]
     if names:
         del step, inp, graph

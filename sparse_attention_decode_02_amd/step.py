@@ -16,6 +16,20 @@ import torch
 from . import lib
 
 
+def group_attention_pays(blocks, row_len, topk, block_rows):
+    """The step's automatic choice of group attention: there are score blocks
+    of 2..8 rows, and none of their rows is longer than 8 x ``topk`` (so a
+    block's rows select overlapping keys and their union stays small).
+    ``blocks`` is the host block plan ([first row, rows] pairs) or None."""
+    if blocks is None or block_rows > 8:
+        return False
+    multi = [(int(b0), int(n)) for b0, n in blocks if n > 1]
+    if not multi:
+        return False
+    longest = max(int(row_len[b0:b0 + n].max()) for b0, n in multi)
+    return longest <= 8 * topk
+
+
 class _Seq:
     """Prepared library calls issued one after another on one stream."""
 
@@ -49,12 +63,15 @@ class DsaStep:
     of the score blocks of several rows (prefill groups, at most 8 rows) over
     the union of their selections on the matrix cores (dsa_group_attn); rows
     from the first of the trailing one-row blocks on (decode rows) keep the
-    vector kernel."""
+    vector kernel. ``group_attn=None`` takes it when the step has such blocks
+    and none of their rows is longer than 8 x top-k, where a group's rows
+    select overlapping keys (measured: a win at 4.25 x top-k, a loss at
+    512 x top-k)."""
 
     def __init__(self, inp, num_splits: int | None = None, block_rows: int = 1,
                  fused: bool | None = False, topk_chunk: int | None = 0,
                  score_buffer_bytes: int | None = None, hist: bool = False,
-                 group_attn: bool = False):
+                 group_attn: bool | None = False):
         wl = inp.wl
         dev = inp.q.device
         self.inp = inp
@@ -110,6 +127,8 @@ class DsaStep:
         # Group attention: the blocks before the trailing one-row blocks.
         self.group_rows = 0
         self.groups = None
+        if group_attn is None:
+            group_attn = group_attention_pays(self.blocks_host, ln, wl.topk, block_rows)
         if group_attn:
             if self.blocks_host is None or block_rows > 8:
                 raise ValueError("group attention needs score blocks of at most 8 rows")

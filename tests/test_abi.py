@@ -66,6 +66,24 @@ def test_plan_blocks_matches_oracle():
             assert np.array_equal(lib.plan_blocks(req, m), O.score_blocks(req, m))
 
 
+def test_group_attention_automatic_choice():
+    """The step takes group attention when it has blocks of 2..8 rows and none
+    of their rows is longer than 8 x top-k (host logic; no launches)."""
+    from sparse_attention_decode_02_amd.step import group_attention_pays
+    # 4 prefill rows on a 1000-key prior context, then 2 decode rows
+    req, ln = lib.plan_rows(np.array([1000, 9000, 50], np.int32), np.array([4, 1, 1], np.int32))
+    blocks = lib.plan_blocks(req, 8)
+    assert group_attention_pays(blocks, ln, 2048, 8)          # longest block row 1004
+    assert not group_attention_pays(blocks, ln, 100, 8)       # 1004 > 800
+    assert not group_attention_pays(None, ln, 2048, 1)        # no blocks
+    assert not group_attention_pays(blocks, ln, 2048, 16)     # blocks wider than a group
+    one = lib.plan_blocks(req, 1)                             # only one-row blocks
+    assert not group_attention_pays(one, ln, 2048, 1)
+    # a long decode row does not count: only rows of multi-row blocks do
+    req2, ln2 = lib.plan_rows(np.array([100, 900000], np.int32), np.array([8, 1], np.int32))
+    assert group_attention_pays(lib.plan_blocks(req2, 8), ln2, 2048, 8)
+
+
 def test_score_width():
     assert lib.score_width([37, 100]) == 128
     assert lib.score_width([64]) == 64

@@ -594,6 +594,27 @@ def test_group_attn_step():
         assert float(np.abs(step.out[r].double().cpu().numpy() - o).max()) <= 2e-2, r
 
 
+def test_group_attn_automatic_choice():
+    """group_attn=None: on where the blocks' rows are short against top-k
+    (same bits as group_attn=True), off where they are long (same bits as
+    the vector kernel)."""
+    short = I.custom(I.decode(), name="prefill_groups_short", hq=64, hkv=8, topk=2048,
+                     prior=(700, 5000, 60, 0, 3000, 9), new=(37, 9, 8, 3, 1, 1), seed=55)
+    inp = _host_inputs(short)
+    auto = run_step(inp, block_rows=8, fused=None, group_attn=None)
+    on = run_step(inp, block_rows=8, fused=None, group_attn=True)
+    assert auto.groups is not None
+    assert torch.equal(auto.out.view(torch.int16), on.out.view(torch.int16))
+    for r in (0, 36, 40, auto.rows - 1):
+        _, _, _, _, o, _ = oracle_row(auto, r)
+        assert float(np.abs(auto.out[r].double().cpu().numpy() - o).max()) <= 2e-2, r
+    inp = _host_inputs(_prefill_groups_wl(seed=54, topk=256))  # rows up to 20006 > 8 x 256
+    auto = run_step(inp, block_rows=8, fused=None, group_attn=None)
+    off = run_step(inp, block_rows=8, fused=None, group_attn=False)
+    assert auto.groups is None
+    assert torch.equal(auto.out.view(torch.int16), off.out.view(torch.int16))
+
+
 def test_group_attn_zero_length_rows():
     """Rows of length 0 inside a group select nothing: output 0, lse -inf,
     and the group's other rows are unaffected."""
