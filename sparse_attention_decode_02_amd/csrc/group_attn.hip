@@ -27,7 +27,8 @@
 //     flight while this one is computed);
 //   * scores: v_mfma_f32_16x16x32_bf16, query rows as A (held in registers),
 //     keys as B; masked keys give -inf; online softmax per query row in
-//     base 2, fp32;
+//     base 2, fp32, against a deferred reference (raised, with a rescale,
+//     only when a score overtakes it by 2^8);
 //   * values: the fp32 probabilities leave the accumulator layout through
 //     LDS and are split exactly into three bf16 terms (p = hi + mid + lo: a
 //     float's 24 significand bits are three bf16 significands), each
@@ -54,6 +55,7 @@ constexpr int kVst = kGaTile + 8;  // transposed V row stride (elements)
 constexpr int kPst = kGaTile + 4;  // probability tile row stride (floats)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kGaSlack = 8.0f;  // log2 headroom of the deferred softmax reference
 
 template <int CTRL>
 __device__ __forceinline__ float dpp_f(float v) {
@@ -323,21 +325,41 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
         const int e = e0 + n * 16 + qrow;
         ok[n] = e < (int)n_u && ((umask[min(e, kGaWin - 1)] >> my_tr) & 1u);
       }
+      // Online softmax against a deferred reference: a row's m is raised to
+      // its running max (and its sum and outputs rescaled) only when a score
+      // overtakes it by more than 2^kGaSlack, so most tiles skip the
+      // rescale; o and the sum share the reference, so the normalized
+      // result is the same and every probability stays <= 2^kGaSlack.
+      bool over = false;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float x = fmaxf(ok[0] ? s[0][i] * scale_log2 : -INFINITY,
+                              ok[1] ? s[1][i] * scale_log2 : -INFINITY);
+        over |= x > m[i] + kGaSlack;
+      }
+      if (__ballot(over) != 0) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const float x = fmaxf(ok[0] ? s[0][i] * scale_log2 : -INFINITY,
+                                ok[1] ? s[1][i] * scale_log2 : -INFINITY);
+          const float mt = row16_max(x);
+          const bool up = mt > m[i] + kGaSlack;
+          // m = -inf (no selected key yet): alpha = 0 clears what is zero.
+          const float alpha = up ? __builtin_amdgcn_exp2f(m[i] - mt) : 1.0f;
+          lsum[i] *= alpha;
+#pragma unroll
+          for (int nt = 0; nt < kGaD / 16; ++nt) o[nt][i] *= alpha;
+          m[i] = up ? mt : m[i];
+        }
+      }
       float pv[2][4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float a0 = ok[0] ? s[0][i] * scale_log2 : -INFINITY;
-        const float a1 = ok[1] ? s[1][i] * scale_log2 : -INFINITY;
-        const float mt = row16_max(fmaxf(a0, a1));
-        const float mn = fmaxf(m[i], mt);
-        // Rows with no selected key yet keep m = -inf and everything zero.
-        const float alpha = mn == -INFINITY ? 1.0f : __builtin_amdgcn_exp2f(m[i] - mn);
-        pv[0][i] = ok[0] ? __builtin_amdgcn_exp2f(a0 - mn) : 0.0f;
-        pv[1][i] = ok[1] ? __builtin_amdgcn_exp2f(a1 - mn) : 0.0f;
-        lsum[i] = lsum[i] * alpha + pv[0][i] + pv[1][i];
-#pragma unroll
-        for (int nt = 0; nt < kGaD / 16; ++nt) o[nt][i] *= alpha;
-        m[i] = mn;
+        // A masked key has probability 0 whatever the reference (before a
+        // row's first selected key m is still -inf).
+        pv[0][i] = ok[0] ? __builtin_amdgcn_exp2f(s[0][i] * scale_log2 - m[i]) : 0.0f;
+        pv[1][i] = ok[1] ? __builtin_amdgcn_exp2f(s[1][i] * scale_log2 - m[i]) : 0.0f;
+        lsum[i] += pv[0][i] + pv[1][i];
       }
       // Probabilities to the A layout through LDS (row l % 16, keys
       // (l / 16) * 8 .. + 8), split into three exact bf16 terms.
