@@ -17,14 +17,16 @@
 //
 // One workgroup of 4 waves per (group, KV head); wave w owns query rows
 // 16w .. 16w + 15, i.e. group rows 2w and 2w + 1, all 8 heads each.
-//   * union: positions are taken in windows of kWin from the smallest one
+//   * union: positions are taken in windows of kGaWin from the smallest one
 //     not yet consumed; every row's selections inside the window (a run of
 //     its ascending list) set their row's bit in an LDS byte map, which is
 //     then compacted in position order into (offset, mask) entries;
 //   * each entry's cache row is resolved through the block table once per
-//     window; tiles of 32 union keys: the 4 waves stage the keys' K rows and
-//     transposed V rows for the KV head in LDS (the next tile's loads in
-//     flight while this one is computed);
+//     window; tiles of 32 union keys: the keys' K and V rows for the KV head
+//     are copied straight from global memory into one of three LDS buffers
+//     (global_load_lds, no registers), the copies of the next two tiles in
+//     flight while one is computed; V stays in row order and its B
+//     fragments are read with the transposing ds_read_b64_tr_b16;
 //   * scores: v_mfma_f32_16x16x32_bf16, query rows as A (held in registers),
 //     keys as B; masked keys give -inf; online softmax per query row in
 //     base 2, fp32, against a deferred reference (raised, with a rescale,
@@ -45,13 +47,21 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kGaThreads = 256;  // 4 waves
-constexpr int kGaWin = 4096;     // positions per union window
+constexpr int kGaWin = 2048;     // positions per union window
+constexpr int kWpt = kGaWin / 4 / kGaThreads;  // byte-map words per thread in the compaction
+static_assert(kWpt >= 1 && kWpt * 4 * kGaThreads == kGaWin, "the compaction covers the window exactly");
 constexpr int kGaTile = 32;      // union keys per tile
 constexpr int kGaRows = 8;       // rows per group, at most
 constexpr int kGaD = 128;        // head dim
 constexpr int kGaG = 8;          // query heads per KV head
-constexpr int kKst = kGaD + 8;   // K tile row stride (elements): B-fragment reads hit distinct banks
-constexpr int kVst = kGaTile + 8;  // transposed V row stride (elements)
+constexpr int kGaStages = 3;     // LDS tile buffers: two tiles' loads in flight, one computed
+// s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
+// 6:4, lgkmcnt 11:8): wait until at most 8, 4 or 0 vector memory
+// instructions are outstanding, nothing else.
+constexpr int kWaitVm8 = 8 | (7 << 4) | (15 << 8);
+constexpr int kWaitVm4 = 4 | (7 << 4) | (15 << 8);
+constexpr int kWaitVm0 = 0 | (7 << 4) | (15 << 8);
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);  // LDS / scalar only
 constexpr int kPst = kGaTile + 4;  // probability tile row stride (floats)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
@@ -81,6 +91,32 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
   if ((u & 0x7FFFFFFFu) > 0x7F800000u) return (uint16_t)((u >> 16) | 0x40u);
   u += 0x7FFFu + ((u >> 16) & 1u);
   return (uint16_t)(u >> 16);
+}
+
+// Tile rows are stored unpadded (256 bytes per key) with the 16 16-byte
+// pieces of key j's row permuted: piece p sits in slot p ^ f(j). For K,
+// f(j) = j % 16 spreads the 16 keys of a B-fragment read over all banks; for
+// V (read with the transposing ds_read_b64_tr_b16, four keys x four dims per
+// 16-lane group) f(j) = 2 (j % 4) + 8 ((j / 8) % 2) does the same.
+__device__ __forceinline__ int k_slot_xor(int j) { return j & 15; }
+__device__ __forceinline__ int v_slot_xor(int j) { return ((j & 3) << 1) | (((j >> 3) & 1) << 3); }
+
+typedef __attribute__((address_space(1))) void ga_gvoid;
+typedef __attribute__((address_space(3))) void ga_lvoid;
+typedef __bf16 bf16x4_t __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) bf16x4_t ga_lds_bf16x4;
+
+// A workgroup barrier without the memory fences of __syncthreads, whose
+// release would wait for every load in flight (the next tiles' copies
+// included). LDS reads and writes on either side stay on their side (the
+// empty asm for the compiler, the scheduling barriers for the backend); the
+// caller waits for whatever the other waves must see.
+__device__ __forceinline__ void ga_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_sched_barrier(0);
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_sched_barrier(0);
+  asm volatile("" ::: "memory");
 }
 
 // Orders this wave's LDS writes before its own later LDS reads.
@@ -123,8 +159,13 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
   __shared__ uint32_t bmap[kGaWin / 4];            // the window's byte map: a row bit per position
   __shared__ uint8_t umask[kGaWin];                // union entry -> its rows' bits
   __shared__ uint32_t urow[kGaWin];                // union entry -> position, then its cache row
-  __shared__ __attribute__((aligned(16))) uint16_t k_lds[kGaTile * kKst];
-  __shared__ __attribute__((aligned(16))) uint16_t v_lds[kGaD * kVst];   // [dim][key]
+  // Tile buffers (K and V of three tiles): [key][128 dims], pieces permuted
+  // per key. Separate arrays, each named where it is used, so that the
+  // compiler can tell a tile's reads from the copies into the other buffers
+  // and waits only for the copies it reads.
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf0[kGaTile * kGaD], vbuf0[kGaTile * kGaD];
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf1[kGaTile * kGaD], vbuf1[kGaTile * kGaD];
+  __shared__ __attribute__((aligned(16))) uint16_t kbuf2[kGaTile * kGaD], vbuf2[kGaTile * kGaD];
   __shared__ __attribute__((aligned(16))) float p_lds[4][16 * kPst];
   __shared__ int cursor[kGaRows];
   __shared__ int nextpos[kGaRows];
@@ -177,38 +218,24 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
   if (tid < kGaRows) cursor[tid] = 0;
   __syncthreads();
 
-  // Staging of one tile. K: thread t takes union entry t / 8 and dims
-  // (t % 8) * 16 .. + 16 (32 bytes). V: thread t takes the key pair
-  // 2 (t % 16), 2 (t % 16) + 1 and dims (t / 16) * 8 .. + 8, and stores each
-  // dim's two keys as one 32-bit word of the transposed tile. Entries past
-  // the union re-read the tile's first key (in bounds; masked).
-  const int st_key = tid >> 3, st_c = tid & 7;
-  const int sv_pair = tid & 15, sv_dim = (tid >> 4) * 8;
-  struct Stage {
-    uint4 k[2], v[2];
-  };
-  auto stage_load = [&](Stage& st, int e, int n_u) {
-    const int ek = e + st_key < n_u ? e + st_key : e;
-    const int ev0 = e + 2 * sv_pair < n_u ? e + 2 * sv_pair : e;
-    const int ev1 = e + 2 * sv_pair + 1 < n_u ? e + 2 * sv_pair + 1 : e;
-    const uint4* ks = reinterpret_cast<const uint4*>(kgroup + (size_t)urow[ek] * kv_stride + st_c * 16);
-    st.k[0] = ks[0];
-    st.k[1] = ks[1];
-    st.v[0] = *reinterpret_cast<const uint4*>(vgroup + (size_t)urow[ev0] * kv_stride + sv_dim);
-    st.v[1] = *reinterpret_cast<const uint4*>(vgroup + (size_t)urow[ev1] * kv_stride + sv_dim);
-  };
-  auto stage_store = [&](const Stage& st) {
-    uint4* kd = reinterpret_cast<uint4*>(k_lds + st_key * kKst + st_c * 16);
-    kd[0] = st.k[0];
-    kd[1] = st.k[1];
-    const uint32_t a[4] = {st.v[0].x, st.v[0].y, st.v[0].z, st.v[0].w};
-    const uint32_t b[4] = {st.v[1].x, st.v[1].y, st.v[1].z, st.v[1].w};
-    uint32_t* vd = reinterpret_cast<uint32_t*>(v_lds) + sv_pair;
+  // A tile's K and V rows go straight from global memory to LDS (no
+  // registers): each of a wave's four load instructions covers four keys'
+  // 256-byte rows, lane l taking piece (l % 16) ^ f(key) of key l / 16, so a
+  // lane's 16 bytes land in slot l % 16. Entries past the union re-read the
+  // tile's first key (in bounds; masked).
+  auto issue_tile = [&](int t, uint16_t* kdst, uint16_t* vdst, int n_u) {
+    const int e0 = t * kGaTile;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      // dims sv_dim + 2w (low halves) and sv_dim + 2w + 1 (high halves)
-      vd[(sv_dim + 2 * w) * (kVst / 2)] = (a[w] & 0xFFFFu) | (b[w] << 16);
-      vd[(sv_dim + 2 * w + 1) * (kVst / 2)] = (a[w] >> 16) | (b[w] & 0xFFFF0000u);
+    for (int u = 0; u < 2; ++u) {
+      const int i = 2 * wave + u;           // keys 4i .. 4i + 3 of the tile
+      const int kk = 4 * i + (lane >> 4);
+      const int sl = lane & 15;
+      const int e = e0 + kk < n_u ? e0 + kk : e0;
+      const size_t row = urow[e];
+      const uint16_t* kp = kgroup + row * kv_stride + 8 * (sl ^ k_slot_xor(kk));
+      const uint16_t* vp = vgroup + row * kv_stride + 8 * (sl ^ v_slot_xor(kk));
+      __builtin_amdgcn_global_load_lds((ga_gvoid*)kp, (ga_lvoid*)(kdst + i * 4 * kGaD), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((ga_gvoid*)vp, (ga_lvoid*)(vdst + i * 4 * kGaD), 16, 0, 0);
     }
   };
 
@@ -262,25 +289,26 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
     }
     __syncthreads();
     // ---- compaction: positions with a bit, in order ----
+    // Thread t owns the kWpt map words from t * kWpt (4 positions a word).
     uint32_t n_u;
     {
-      uint32_t wds[4];
+      uint32_t wds[kWpt];
       uint32_t cnt = 0;
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        wds[u] = bmap[tid * 4 + u];
+      for (int u = 0; u < kWpt; ++u) {
+        wds[u] = bmap[tid * kWpt + u];
 #pragma unroll
         for (int b = 0; b < 4; ++b) cnt += ((wds[u] >> (8 * b)) & 0xFFu) != 0u;
       }
       uint32_t o = ga_block_scan(cnt, scan_sh[0], &n_u);
 #pragma unroll
-      for (int u = 0; u < 4; ++u)
+      for (int u = 0; u < kWpt; ++u)
 #pragma unroll
         for (int b = 0; b < 4; ++b) {
           const uint32_t msk = (wds[u] >> (8 * b)) & 0xFFu;
           if (msk) {
             umask[o] = (uint8_t)msk;
-            urow[o] = (uint32_t)(w0 + tid * 16 + u * 4 + b);
+            urow[o] = (uint32_t)(w0 + tid * 4 * kWpt + u * 4 + b);
             ++o;
           }
         }
@@ -295,17 +323,26 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
     __syncthreads();
 
     // ---- tiles of the window's union ----
-    // The next tile's K and V loads are in flight (registers) while this
-    // tile is computed; every wave reads the tile in LDS, so a barrier closes
-    // each tile before the next is stored.
+    // Tile t is computed from buffer t % 3 while the loads of tiles t + 1
+    // and t + 2 are in flight; a wave's own loads of tile t are complete
+    // when at most the later tiles' instructions (4 per tile) are
+    // outstanding, and a barrier then covers every wave's. A second barrier
+    // closes each tile before its buffer is loaded again.
     const int ntiles = ((int)n_u + kGaTile - 1) / kGaTile;
-    Stage st;
-    stage_load(st, 0, (int)n_u);
-    stage_store(st);
-    __syncthreads();
-    for (int t = 0; t < ntiles; ++t) {
+    // One tile: wait for its copies (and let those of the next two fly),
+    // compute it from (k_lds, v_lds), then close it before its buffers are
+    // reused.
+    auto tile = [&](int t, const uint16_t* k_lds, const uint16_t* v_lds, auto&& issue_ahead) {
       const int e0 = t * kGaTile;
-      if (t + 1 < ntiles) stage_load(st, e0 + kGaTile, (int)n_u);
+      if (t + 2 < ntiles) {
+        issue_ahead();
+        __builtin_amdgcn_s_waitcnt(kWaitVm8);
+      } else if (t + 1 < ntiles) {
+        __builtin_amdgcn_s_waitcnt(kWaitVm4);
+      } else {
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+      }
+      ga_barrier();  // every wave's copies of tile t are in LDS
       // Scores: 16 query rows x 32 keys.
       f32x4_t s[2];
 #pragma unroll
@@ -313,8 +350,9 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
         s[n] = f32x4_t{};
 #pragma unroll
         for (int kk = 0; kk < kGaD / 32; ++kk) {
+          const int key = n * 16 + qrow;
           const bf16x8_t kb = *reinterpret_cast<const bf16x8_t*>(
-              k_lds + (n * 16 + qrow) * kKst + kk * 32 + kgrp * 8);
+              k_lds + key * kGaD + 8 * ((kk * 4 + kgrp) ^ k_slot_xor(key)));
           s[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], kb, s[n], 0, 0, 0);
         }
       }
@@ -390,20 +428,42 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
         pm = __builtin_bit_cast(bf16x8_t, mb);
         pl = __builtin_bit_cast(bf16x8_t, lb);
       }
-      // Values: O[16 x 128] += P[16 x 32] . V[32 x 128], three terms.
+      // Values: O[16 x 128] += P[16 x 32] . V[32 x 128], three terms. The B
+      // fragment (dim nt * 16 + l % 16, keys (l / 16) * 8 .. + 8) comes from
+      // two transposing reads: lane j of a 16-lane group addresses the four
+      // dims nt * 16 + 4 (j % 4) .. + 4 of key (l / 16) * 8 + j / 4 (+ 4), and
+      // lane m receives dim nt * 16 + m of the four keys.
+      const int jq = qrow & 3, jk = qrow >> 2;
 #pragma unroll
       for (int nt = 0; nt < kGaD / 16; ++nt) {
-        const bf16x8_t vb = *reinterpret_cast<const bf16x8_t*>(
-            v_lds + (nt * 16 + qrow) * kVst + kgrp * 8);
+        bf16x4_t vh[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int key = kgrp * 8 + hh * 4 + jk;
+          const int d = nt * 16 + 4 * jq;
+          const uint16_t* src = v_lds + key * kGaD + 8 * ((d >> 3) ^ v_slot_xor(key)) + (d & 7);
+          vh[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (ga_lds_bf16x4*)(__attribute__((address_space(3))) uint16_t*)src);
+        }
+        const bf16x8_t vb = {vh[0][0], vh[0][1], vh[0][2], vh[0][3],
+                             vh[1][0], vh[1][1], vh[1][2], vh[1][3]};
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, o[nt], 0, 0, 0);
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pm, vb, o[nt], 0, 0, 0);
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, o[nt], 0, 0, 0);
       }
-      __syncthreads();
-      if (t + 1 < ntiles) {
-        stage_store(st);
-        __syncthreads();
-      }
+      // Every wave's reads of this tile's buffers are done (their MFMAs have
+      // issued) before any wave copies a later tile into them.
+      __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+      ga_barrier();
+    };
+    issue_tile(0, kbuf0, vbuf0, (int)n_u);
+    if (1 < ntiles) issue_tile(1, kbuf1, vbuf1, (int)n_u);
+    for (int t = 0; t < ntiles; t += 3) {
+      tile(t, kbuf0, vbuf0, [&] { issue_tile(t + 2, kbuf2, vbuf2, (int)n_u); });
+      if (t + 1 >= ntiles) break;
+      tile(t + 1, kbuf1, vbuf1, [&] { issue_tile(t + 3, kbuf0, vbuf0, (int)n_u); });
+      if (t + 2 >= ntiles) break;
+      tile(t + 2, kbuf2, vbuf2, [&] { issue_tile(t + 4, kbuf1, vbuf1, (int)n_u); });
     }
     // The next window rebuilds the byte map and the union list after this
     // barrier (every read of them is done).
