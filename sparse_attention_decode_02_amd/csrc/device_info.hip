@@ -46,6 +46,24 @@ int cus_locked(int dev) {
 
 }  // namespace
 
+const SideStream* side_stream() {
+  static SideStream g_side[kMaxDevices];
+  static bool g_side_ok[kMaxDevices];
+  const int dev = current_device();
+  if (dev < 0) return nullptr;
+  std::lock_guard<std::mutex> lock(g_mutex);
+  if (!g_side_ok[dev]) {
+    SideStream s{};
+    if (hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) != hipSuccess) return nullptr;
+    if (hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&s.join, hipEventDisableTiming) != hipSuccess)
+      return nullptr;
+    g_side[dev] = s;
+    g_side_ok[dev] = true;
+  }
+  return &g_side[dev];
+}
+
 int device_cus() {
   const int dev = current_device();
   if (dev < 0) return 0;

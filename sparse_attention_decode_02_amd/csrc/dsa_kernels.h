@@ -16,6 +16,16 @@ int device_capacity(const void* kernel, int block);
 // HIP error.
 int device_cus();
 
+// A second stream of the current device (non-blocking, default priority) with
+// a fork and a join event, made once and kept: a launcher records `fork` on
+// its stream, has this stream wait for it, enqueues independent work here,
+// records `join` and has its own stream wait for that. Null on a HIP error.
+struct SideStream {
+  hipStream_t stream;
+  hipEvent_t fork, join;
+};
+const SideStream* side_stream();
+
 // Keys a workgroup of the bf16 indexer covers for one row (a multiple of 64):
 // the chunks of all blocks fill the device about once, at most 2048 keys.
 int indexer_chunk_keys(int num_blocks, int width, int num_heads, int head_dim, bool full);

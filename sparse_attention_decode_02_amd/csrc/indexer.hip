@@ -530,6 +530,39 @@ hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kc
   const auto* q = static_cast<const uint16_t*>(q_idx);
   const auto* k = static_cast<const uint16_t*>(kcache);
   const bool with_block_kernel = blocks && indexer_uses_blocks(rows, num_blocks);
+  // Beside the block kernel (matrix-core bound) the row kernel (HBM bound)
+  // runs on a second stream, so the two share the compute units.
+  const SideStream* side = with_block_kernel ? side_stream() : nullptr;
+  if (with_block_kernel && !side) return hipErrorOutOfMemory;
+  hipStream_t row_stream = stream;
+  if (side) {
+    hipError_t e = hipEventRecord(side->fork, stream);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->fork, 0);
+    if (e != hipSuccess) return e;
+    row_stream = side->stream;
+  }
+  {
+    const int single_only = with_block_kernel ? 1 : 0;
+    const int chunk = indexer_chunk_keys(num_blocks, width, num_heads, head_dim, full);
+    const int chunks = (width + chunk - 1) / chunk;
+    const int total = num_blocks * chunks;
+#define DSA_IDX_LAUNCH(HT, DI)                                                                 \
+  hipLaunchKernelGGL((indexer_mfma_kernel<HT, DI>),                                            \
+                     dim3(single_only ? xcd_grouped_grid(total, 2) : total), dim3(kIdxThreads), 0, \
+                     row_stream,                                                               \
+                     q, w, k, bt, row_req, row_len, blocks, scores, width, page_shift,         \
+                     max_pages, chunk, chunks, total, score_row0, single_only,                 \
+                     with_block_kernel ? nullptr : hist)
+    if (num_heads == 64 && head_dim == 128) DSA_IDX_LAUNCH(4, 128);
+    else if (num_heads == 32 && head_dim == 128) DSA_IDX_LAUNCH(2, 128);
+    else if (num_heads == 64 && head_dim == 64) DSA_IDX_LAUNCH(4, 64);
+    else if (num_heads == 32 && head_dim == 64) DSA_IDX_LAUNCH(2, 64);
+    else return hipErrorInvalidValue;
+#undef DSA_IDX_LAUNCH
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess && side) e = hipEventRecord(side->join, side->stream);
+    if (e != hipSuccess) return e;
+  }
   if (with_block_kernel) {
     const int chunk = indexer_block_chunk_keys(num_blocks, width, num_heads, head_dim, full);
     const int total = num_blocks * ((width + chunk - 1) / chunk);
@@ -544,29 +577,13 @@ hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kc
     else if (num_heads == 32 && head_dim == 64) DSA_IDX_BLK(2, 64);
     else return hipErrorInvalidValue;
 #undef DSA_IDX_BLK
-    const hipError_t e = hipGetLastError();
+    hipError_t e = hipGetLastError();
+    if (e == hipSuccess) e = hipStreamWaitEvent(stream, side->join, 0);
     if (e != hipSuccess) return e;
   }
-  const int single_only = with_block_kernel ? 1 : 0;
-  const int chunk = indexer_chunk_keys(num_blocks, width, num_heads, head_dim, full);
-  const int chunks = (width + chunk - 1) / chunk;
-  const int total = num_blocks * chunks;
-#define DSA_IDX_LAUNCH(HT, DI)                                                                 \
-  hipLaunchKernelGGL((indexer_mfma_kernel<HT, DI>),                                            \
-                     dim3(single_only ? xcd_grouped_grid(total, 2) : total), dim3(kIdxThreads), 0, \
-                     stream,                                                                   \
-                     q, w, k, bt, row_req, row_len, blocks, scores, width, page_shift,         \
-                     max_pages, chunk, chunks, total, score_row0, single_only,                 \
-                     with_block_kernel ? nullptr : hist)
-  if (num_heads == 64 && head_dim == 128) DSA_IDX_LAUNCH(4, 128);
-  else if (num_heads == 32 && head_dim == 128) DSA_IDX_LAUNCH(2, 128);
-  else if (num_heads == 64 && head_dim == 64) DSA_IDX_LAUNCH(4, 64);
-  else if (num_heads == 32 && head_dim == 64) DSA_IDX_LAUNCH(2, 64);
-  else return hipErrorInvalidValue;
-#undef DSA_IDX_LAUNCH
-  hipError_t e = hipGetLastError();
+  hipError_t e = hipSuccess;
   // Rows scored by the block kernel are counted from their written scores.
-  if (e == hipSuccess && hist && with_block_kernel)
+  if (hist && with_block_kernel)
     e = launch_score_hist(scores, row_len, rows, width, hist, false, stream);
   return e;
 }

@@ -723,14 +723,17 @@ def test_block_indexer_matches_row_kernel(hi, di, page):
         assert bool((blk.scores[r].view(torch.int32) == CANARY).all())
 
 
+@pytest.mark.parametrize("block_rows", [1, 8], ids=["rows", "blocks"])
 @pytest.mark.parametrize("fused", [True, False], ids=["fused", "two-launch"])
-def test_graph_replay_matches_eager(fused):
+def test_graph_replay_matches_eager(fused, block_rows):
     """The step recorded into a HIP graph and replayed gives the eager step's
     bits on every replay, with eager work in between, and follows row lengths
-    changed in device memory between replays (same width)."""
-    _say(f"graph replay, fused {fused}")
+    changed in device memory between replays (same width). With score blocks
+    the block and row indexer kernels run on two streams, forked and joined
+    inside the recording."""
+    _say(f"graph replay, fused {fused}, block_rows {block_rows}")
     inp = _host_inputs(_small_mixed(seed=17))
-    step = DsaStep(inp, num_splits=4, fused=fused)
+    step = DsaStep(inp, num_splits=4, fused=fused, block_rows=block_rows)
     outs = lambda: [t.clone() for t in (step.scores, step.idx, step.out, step.out_lse)]
 
     def same(a, b):
