@@ -82,6 +82,20 @@ def profiled_traffic(stage, workload_name):
     return None
 
 
+def attention_label(step):
+    """Which attention kernels the step runs: bf16 rows with d 128 and eight
+    query heads per KV group go to the matrix-core kernel, other shapes to
+    the vector kernel; prefill score blocks may go to group attention."""
+    wl = step.wl
+    kern = ("matrix-core kernel" if wl.dtype == "bf16" and wl.d == 128 and wl.hq == 8 * wl.hkv
+            else "vector kernel")
+    merge = "fused merge" if step.fused else "separate merge"
+    if step.groups is not None:
+        return (f"prefill groups over the union of their selections (matrix cores), "
+                f"{step.rows - step.group_rows} rows on the {kern}, {merge}")
+    return f"{kern}, {merge}"
+
+
 def _events(torch):
     return torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
 
@@ -304,10 +318,7 @@ def measure_configs(names, steps, warmup, torch):
                "frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),
                "kernels_us": {n: round(v, 2) for n, v in kern.items()},
                "attention_splits": step.num_splits,
-               "attention": ("prefill groups over the union of their selections (matrix "
-                             f"cores), {step.rows - step.group_rows} rows on the vector kernel"
-                             if step.groups is not None else "vector kernel, fused merge"
-                             if step.fused else "vector kernel, separate merge"),
+               "attention": attention_label(step),
                "topk_mode": ("from the indexer's score histogram" if step.use_hist else
                              f"two-stage, {step.topk_chunk}-position segments"
                              if step.topk_chunk else "one pass")}
@@ -500,9 +511,7 @@ def main(argv=None):
                           f"two-stage, {step.topk_chunk}-position segments" if step.topk_chunk
                           else "one pass"),
             "score_rows_per_window": step.window_rows,
-            "attention": ("prefill groups over the union of their selections (matrix cores), "
-                          f"{step.rows - step.group_rows} rows on the vector kernel"
-                          if step.groups is not None else "vector kernel"),
+            "attention": attention_label(step),
         },
         "hbm_gbps": round(gbps, 1),
         "layer_frac_of_hbm_peak": round(gbps / HBM_PEAK_GBPS, 4),

@@ -413,9 +413,9 @@ int dsa_sparse_attn_splits(int rows, int num_q_heads, int num_kv_heads, int head
  *   out_lse  device [rows][num_q_heads] float32 (output), or NULL
  *
  * Supported: as dsa_sparse_attn, with num_splits in {1, 2, 4, 6, 8} and
- * num_splits <= k; out 16-byte aligned. (Six splits of any shape, and eight
- * splits of bf16 rows with head_dim 128 and eight query heads per KV group,
- * run two pairs per workgroup; the result does not depend on it.)
+ * num_splits <= k; out 16-byte aligned. (Six splits of any shape, and four
+ * or eight splits of bf16 rows with head_dim 128 and eight query heads per
+ * KV group, run two pairs per workgroup; the result does not depend on it.)
  * ------------------------------------------------------------------------ */
 int dsa_sparse_attn_merged(const void* q, const void* k_cache, const void* v_cache,
                            const int32_t* block_table, const int32_t* row_req, const int32_t* idx,
@@ -462,9 +462,12 @@ int dsa_group_attn(const void* q, const void* k_cache, const void* v_cache,
                    float scale, void* out, float* out_lse, dsa_dtype dtype, void* stream);
 
 /* dsa_sparse_attn_merged_splits: a num_splits for dsa_sparse_attn_merged
- * with these shapes on the current device: 6 when rows x KV groups x 6 waves
- * fill the device in about one round, else dsa_sparse_attn_splits rounded
- * down to 1, 2, 4 or 8. Errors as for dsa_sparse_attn_splits. */
+ * with these shapes on the current device. bf16 rows with head_dim 128 and
+ * eight query heads per KV group (the matrix-core kernel): the smallest of
+ * 1, 2, 4, 8 that puts about seven waves (rows x KV groups x splits) on
+ * every compute unit, at most k / 16. Other shapes: 6 when rows x KV groups
+ * x 6 waves fill the device in about one round, else dsa_sparse_attn_splits
+ * rounded down to 1, 2, 4 or 8. Errors as for dsa_sparse_attn_splits. */
 int dsa_sparse_attn_merged_splits(int rows, int num_q_heads, int num_kv_heads, int head_dim,
                                   int k, dsa_dtype dtype, int* num_splits);
 

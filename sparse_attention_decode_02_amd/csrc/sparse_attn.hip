@@ -905,7 +905,12 @@ static hipError_t launch_merged_t(const void* q, const void* kc, const void* vc,
   switch (S) {
     case 1: DSA_MERGED(1, 1);
     case 2: DSA_MERGED(2, 1);
-    case 4: DSA_MERGED(4, 1);
+    case 4:
+      // On the matrix-core kernel two pairs (8 waves, 82 KB of LDS) take a
+      // CU each, which spreads a batch of 2 x CUs pairs evenly (~1% faster
+      // than one pair per workgroup, where some CUs hold three).
+      if (sizeof(T) == 2 && d == 128 && hq == 8 * hkv) DSA_MERGED(4, 2);
+      DSA_MERGED(4, 1);
     case 6: DSA_MERGED(6, kPairs6);
     case 8:
       // On the matrix-core kernel two pairs (16 waves) fit a workgroup.
@@ -933,11 +938,11 @@ hipError_t launch_sparse_attn_merged(const void* q, const void* kc, const void* 
 }
 
 int merged_default_splits(int rows, int hq, int hkv, int d, int k, bool bf16) {
-  // Eight splits (matrix-core kernel) or six (vector kernel) in workgroups
-  // of two pairs when that fills the device in about one round at four or
-  // three waves per SIMD (the rows x KV groups are many, the occupancy
-  // allows it); otherwise the split kernel's suggestion rounded down to a
-  // supported workgroup size (1, 2, 4 or 8 waves).
+  // Vector kernel: six splits in workgroups of two pairs when that fills the
+  // device in about one round at three waves per SIMD (the rows x KV groups
+  // are many, the occupancy allows it); otherwise the split kernel's
+  // suggestion rounded down to a supported workgroup size (1, 2, 4 or 8
+  // waves).
   const long long pairs = (long long)rows * hkv;
   const void* kern = bf16 ? attn_kernel_ptr<uint16_t>(d, hq / hkv)
                           : attn_kernel_ptr<float>(d, hq / hkv);
@@ -947,11 +952,17 @@ int merged_default_splits(int rows, int hq, int hkv, int d, int k, bool bf16) {
     cus = 256;
     cap = 3072;
   }
-  // The matrix-core shape: eight splits, two pairs per 16-wave workgroup,
-  // when the batch fills between half the device's wave slots and two rounds.
-  if (bf16 && d == 128 && hq == 8 * hkv && cap / cus == 16 && k >= 8 * 16 && pairs * 8 * 2 >= cap &&
-      pairs * 8 <= 2LL * cap)
-    return 8;
+  if (bf16 && d == 128 && hq == 8 * hkv) {
+    // Matrix-core kernel: the fewest splits (the longest walk per wave, each
+    // wave paying the position -> row prologue and its share of the merge
+    // once) that still put about seven waves on every CU. At 64 rows x 8
+    // groups four splits (8 waves per CU) run ~4% faster than six or eight;
+    // two (4 waves per CU) run 35% slower.
+    int s = 1;
+    while (s < 8 && pairs * s < 7LL * cus) s *= 2;
+    while (s > 1 && s * 16 > k) s /= 2;  // at least one 16-token tile per split
+    return s;
+  }
   if (cap / cus == 12 && k >= 6 * 32 && pairs * 6 <= cap && pairs * 6 * 2 >= cap) return 6;
   const int s = attn_default_splits(rows, hq, hkv, d, k, bf16);
   int f = 1;
