@@ -459,7 +459,6 @@ typedef __attribute__((address_space(1))) void mx_gvoid;
 typedef __attribute__((address_space(3))) void mx_lvoid;
 typedef __attribute__((address_space(3))) mx_bf16x4 mx_lds_bf16x4;
 constexpr int kMxTile = 16;   // tokens per tile
-constexpr int kMxSpan = 256;  // slots resolved to cache rows at once
 // s_waitcnt immediate (gfx9 encoding): no vector memory instruction
 // outstanding; LDS, scalar and export counters not waited on.
 constexpr int kMxWaitVm0 = 0 | (7 << 4) | (15 << 8);
@@ -501,7 +500,12 @@ __global__ __launch_bounds__(64 * (FS > 0 ? FS * PP : 1), 4) void sparse_attn_mx
   constexpr int NW = FS > 0 ? FS * PP : 1;  // waves per workgroup
   __shared__ __attribute__((aligned(16))) uint16_t kbuf[NW][kMxTile * D];
   __shared__ __attribute__((aligned(16))) uint16_t vbuf[NW][kMxTile * D];
-  __shared__ uint32_t rows_all[NW][kMxSpan];
+  // Slots resolved to cache rows at once: a whole split up to 512 (one
+  // prologue per wave at four splits of 2048), 256 in 16-wave workgroups
+  // (the LDS holds no more).
+  constexpr int SPAN = NW <= 8 ? 512 : 256;
+  constexpr int RPL = SPAN / 64;
+  __shared__ uint32_t rows_all[NW][SPAN];
   // Each pair's query block as 16 head rows (rows G..15 zero: the padding
   // columns of the score tiles), rows padded so a fragment read spreads over
   // the banks.
@@ -532,6 +536,18 @@ __global__ __launch_bounds__(64 * (FS > 0 ? FS * PP : 1), 4) void sparse_attn_mx
   const uint16_t* vgroup = vc + (size_t)g * D;
   const bool head_lane = tl < G;
 
+  // The first span's selected positions are requested before the query
+  // block, so that the two loads' latencies overlap.
+  int pos[RPL];
+  auto load_pos = [&](int c0, int n) {
+#pragma unroll
+    for (int u = 0; u < RPL; ++u) {
+      const int i = lane + 64 * u;
+      pos[u] = i < n ? ir[c0 + i] : -1;
+    }
+  };
+  load_pos(a, min(b - a, SPAN));
+
   // The waves of a pair load its query block together (a dead pair's waves
   // write zeros).
   {
@@ -552,16 +568,10 @@ __global__ __launch_bounds__(64 * (FS > 0 ? FS * PP : 1), 4) void sparse_attn_mx
 #pragma unroll
   for (int nt = 0; nt < D / 16; ++nt) o[nt] = mx_f32x4{0.0f, 0.0f, 0.0f, 0.0f};
 
-  for (int c0 = a; c0 < b; c0 += kMxSpan) {
-    const int n = min(b - c0, kMxSpan);
+  for (int c0 = a; c0 < b; c0 += SPAN) {
+    const int n = min(b - c0, SPAN);
     wave_sync();  // this wave's previous span readers are done with rows_lds
-    constexpr int RPL = kMxSpan / 64;
-    int pos[RPL];
-#pragma unroll
-    for (int u = 0; u < RPL; ++u) {
-      const int i = lane + 64 * u;
-      pos[u] = i < n ? ir[c0 + i] : -1;
-    }
+    if (c0 != a) load_pos(c0, n);
     uint32_t prow[RPL];
 #pragma unroll
     for (int u = 0; u < RPL; ++u)

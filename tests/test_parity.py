@@ -99,10 +99,11 @@ def test_split_counts(S):
 
 @pytest.mark.parametrize("S,fused", [(1, False), (3, False), (1, True), (2, True)])
 def test_attention_splits_over_several_spans(S, fused):
-    """Splits of more than 256 slots: the attention kernels resolve a split's
-    positions to cache rows 256 at a time (the matrix-core kernel) or 512 at
-    a time (the vector kernel), so these walk several spans, the last one
-    partial, with short rows' padding in the later spans."""
+    """Splits of more than 512 slots: the attention kernels resolve a split's
+    positions to cache rows 256 or 512 at a time (the matrix-core kernel, by
+    workgroup size) or 512 at a time (the vector kernel), so these walk
+    several spans, the last one partial, with short rows' padding in the
+    later spans."""
     _say(f"attention over several spans, splits {S}, fused {fused}")
     step = run_step(_host_inputs(_small_mixed(seed=61, topk=1024)), num_splits=S, fused=fused)
     e = _check_all(step)
