@@ -46,9 +46,10 @@ int cus_locked(int dev) {
 
 }  // namespace
 
-const SideStream* side_stream() {
+SideStream* side_stream() {
   static SideStream g_side[kMaxDevices];
   static bool g_side_ok[kMaxDevices];
+  static std::mutex g_side_lock[kMaxDevices];
   const int dev = current_device();
   if (dev < 0) return nullptr;
   std::lock_guard<std::mutex> lock(g_mutex);
@@ -58,6 +59,7 @@ const SideStream* side_stream() {
     if (hipEventCreateWithFlags(&s.fork, hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&s.join, hipEventDisableTiming) != hipSuccess)
       return nullptr;
+    s.lock = &g_side_lock[dev];
     g_side[dev] = s;
     g_side_ok[dev] = true;
   }

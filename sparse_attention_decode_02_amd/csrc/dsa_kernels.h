@@ -4,6 +4,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <mutex>
 #include <stdint.h>
 
 namespace dsa {
@@ -19,12 +20,15 @@ int device_cus();
 // A second stream of the current device (non-blocking, default priority) with
 // a fork and a join event, made once and kept: a launcher records `fork` on
 // its stream, has this stream wait for it, enqueues independent work here,
-// records `join` and has its own stream wait for that. Null on a HIP error.
+// records `join` and has its own stream wait for that -- all while holding
+// `lock`, so that launchers on several host threads never wait on each
+// other's event records. Null on a HIP error.
 struct SideStream {
   hipStream_t stream;
   hipEvent_t fork, join;
+  std::mutex* lock;
 };
-const SideStream* side_stream();
+SideStream* side_stream();
 
 // Keys a workgroup of the bf16 indexer covers for one row (a multiple of 64):
 // the chunks of all blocks fill the device about once, at most 2048 keys.

@@ -532,8 +532,10 @@ hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kc
   const bool with_block_kernel = blocks && indexer_uses_blocks(rows, num_blocks);
   // Beside the block kernel (matrix-core bound) the row kernel (HBM bound)
   // runs on a second stream, so the two share the compute units.
-  const SideStream* side = with_block_kernel ? side_stream() : nullptr;
+  SideStream* side = with_block_kernel ? side_stream() : nullptr;
   if (with_block_kernel && !side) return hipErrorOutOfMemory;
+  std::unique_lock<std::mutex> side_lock;
+  if (side) side_lock = std::unique_lock<std::mutex>(*side->lock);
   hipStream_t row_stream = stream;
   if (side) {
     hipError_t e = hipEventRecord(side->fork, stream);
