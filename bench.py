@@ -296,15 +296,16 @@ def measure_configs(names, steps, warmup, torch):
     out = {}
     for spec in names:
         name, _, opt = spec.partition("+")
-        hist = opt == "hist"
+        # the step's automatic top-k, or the histogram selection forced on / off
+        hist = True if opt == "hist" else False if opt == "onepass" else None
         # the step's automatic choice, or group attention forced on / off
         group = True if opt == "group" else False if opt == "vector" else None
         wl = I.WORKLOADS[name]()
-        print(f"[bench] config {wl.name}{' (histogram top-k)' if hist else ''}"
+        print(f"[bench] config {wl.name}{' (histogram top-k)' if hist else ' (one-pass top-k)' if hist is False else ''}"
               f"{' (group attention)' if group else ' (vector attention)' if group is False else ''}",
               file=sys.stderr, flush=True)
         inp = I.generate(wl, "cuda")
-        step = DsaStep(inp, block_rows=8, fused=None, topk_chunk=0 if hist else None, hist=hist,
+        step = DsaStep(inp, block_rows=8, fused=None, topk_chunk=0 if hist is not None else None, hist=hist,
                        group_attn=group)
         torch.cuda.synchronize()
         ms = time_steps(step, steps, warmup, torch)
@@ -387,9 +388,10 @@ def main(argv=None):
     ap.add_argument("--score-buffer-mib", type=int, default=0,
                     help="score and select in row windows through a buffer of this many MiB "
                          "(0 = every row at once)")
-    ap.add_argument("--hist", type=int, default=0,
+    ap.add_argument("--hist", type=int, default=-1,
                     help="1: the indexer counts each row's scores and the top-k starts from the "
-                         "counts (dsa_indexer_scores_hist + dsa_topk_hist)")
+                         "counts (dsa_indexer_scores_hist + dsa_topk_hist); 0: the one-pass or "
+                         "two-stage top-k; -1 (default): the step's automatic choice")
     ap.add_argument("--group-attn", type=int, default=-1,
                     help="1: attention of multi-row score blocks over the union of their "
                          "selections on the matrix cores (dsa_group_attn); 0: every row on the "
@@ -399,9 +401,10 @@ def main(argv=None):
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="oracle time budget for cpu_baseline, per core setting (0 = skip)")
     ap.add_argument("--configs",
-                    default="tiny,decode,ragged,mixed,ragged+hist,mixed+vector,long,long+hist",
+                    default="tiny,decode,ragged,mixed,ragged+onepass,mixed+vector,long,long+hist",
                     help="other workloads measured in the same run (comma list, '' = none; "
-                         "name+hist: with the histogram top-k)")
+                         "name+hist / name+onepass: with the histogram top-k forced on / off; "
+                         "name+group / name+vector: group attention forced on / off)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the step, run a plain device copy of this many MiB "
                          "(calibrates HBM byte counters)")
@@ -439,7 +442,7 @@ def main(argv=None):
                 fused=False if args.unfused else None,
                 topk_chunk=None if args.topk_chunk < 0 else args.topk_chunk,
                 score_buffer_bytes=(args.score_buffer_mib << 20) if args.score_buffer_mib else None,
-                hist=bool(args.hist),
+                hist=None if args.hist < 0 else bool(args.hist),
                 group_attn=None if args.group_attn < 0 else bool(args.group_attn))
     step = DsaStep(inp, **opts)
     torch.cuda.synchronize()
@@ -541,7 +544,8 @@ def main(argv=None):
     if args.cpu_seconds > 0:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds, torch)
-    this = args.workload + ("+hist" if args.hist else "+group" if args.group_attn > 0
+    this = args.workload + ("+hist" if args.hist > 0 else "+onepass" if args.hist == 0
+                            else "+group" if args.group_attn > 0
                             else "+vector" if args.group_attn == 0 else "")
     names = [n for n in args.configs.split(",") if n and n != this]
     if names:

@@ -30,6 +30,28 @@ def group_attention_pays(blocks, row_len, topk, block_rows):
     return longest <= 8 * topk
 
 
+# Rows longer than this do not fit the one-pass top-k's 32 keys per thread of
+# a 1024-thread workgroup; it then holds 64 per thread and its radix passes
+# cost twice as much, where the histogram selection only ranks the keys at
+# or above the threshold bin.
+ONE_PASS_RESIDENT_KEYS = 32768
+
+
+def histogram_topk_pays(blocks, row_len, one_pass):
+    """The step's automatic choice of the histogram top-k (dsa_indexer_scores_hist
+    + dsa_topk_hist): the selection runs in one pass (no score windows, no
+    two stages), no score block holds more than one row (the block indexer
+    would need a separate counting pass over the written scores), and some
+    row is longer than ``ONE_PASS_RESIDENT_KEYS``. Measured: ragged batch 64
+    x 1..65536 193 -> 179 us; it loses at 32768 keys (+0.7 us), on a mixed
+    step with prefill blocks (+170 us) and at decode batch 8 (+2 us)."""
+    if not one_pass or len(row_len) == 0:
+        return False
+    if blocks is not None and any(int(n) > 1 for _, n in blocks):
+        return False
+    return int(row_len.max()) > ONE_PASS_RESIDENT_KEYS
+
+
 class _Seq:
     """Prepared library calls issued one after another on one stream."""
 
@@ -59,7 +81,8 @@ class DsaStep:
     indexer count each row's scores by the top bits of their order keys
     (dsa_indexer_scores_hist) and the top-k start from those counts
     (dsa_topk_hist), which leaves them cleared for the next run; it excludes
-    score windows and the two-stage top-k. ``group_attn`` runs the attention
+    score windows and the two-stage top-k; ``hist=None`` takes it where
+    ``histogram_topk_pays`` finds it faster. ``group_attn`` runs the attention
     of the score blocks of several rows (prefill groups, at most 8 rows) over
     the union of their selections on the matrix cores (dsa_group_attn); rows
     from the first of the trailing one-row blocks on (decode rows) keep the
@@ -70,7 +93,7 @@ class DsaStep:
 
     def __init__(self, inp, num_splits: int | None = None, block_rows: int = 1,
                  fused: bool | None = False, topk_chunk: int | None = 0,
-                 score_buffer_bytes: int | None = None, hist: bool = False,
+                 score_buffer_bytes: int | None = None, hist: bool | None = False,
                  group_attn: bool | None = False):
         wl = inp.wl
         dev = inp.q.device
@@ -100,7 +123,6 @@ class DsaStep:
         self.window_rows = self.rows
         if score_buffer_bytes is not None:
             self.window_rows = min(self.rows, lib.select_window_rows(self.width, score_buffer_bytes))
-        self.use_hist = hist
         if hist and (score_buffer_bytes is not None or topk_chunk):
             raise ValueError("the histogram top-k does not combine with score windows or two stages")
         if hist:
@@ -109,6 +131,10 @@ class DsaStep:
             # The suggestion for a window's rows, at the batch's fill.
             window_keys = self.total_keys * self.window_rows // max(1, self.rows)
             topk_chunk = lib.topk_chunk_suggest(self.window_rows, self.width, wl.topk, window_keys)
+        if hist is None:
+            hist = histogram_topk_pays(self.blocks_host, ln,
+                                       score_buffer_bytes is None and not topk_chunk)
+        self.use_hist = hist
         self.topk_chunk = topk_chunk
         self.windowed = score_buffer_bytes is not None
         self.scores = torch.empty(self.window_rows, self.width, dtype=torch.float32, device=dev)

@@ -84,6 +84,24 @@ def test_group_attention_automatic_choice():
     assert group_attention_pays(lib.plan_blocks(req2, 8), ln2, 2048, 8)
 
 
+def test_histogram_topk_automatic_choice():
+    """The step takes the histogram top-k when it selects in one pass, has no
+    multi-row score blocks and some row is longer than the one-pass kernel
+    holds at 32 keys per thread (host logic; no launches)."""
+    from sparse_attention_decode_02_amd.step import ONE_PASS_RESIDENT_KEYS, histogram_topk_pays
+    assert ONE_PASS_RESIDENT_KEYS == 32768
+    req, ln = lib.plan_rows(np.array([65535, 2000, 40], np.int32), np.array([1, 1, 1], np.int32))
+    assert histogram_topk_pays(None, ln, True)                       # a 65536-key decode row
+    assert histogram_topk_pays(lib.plan_blocks(req, 8), ln, True)    # one-row blocks only
+    assert not histogram_topk_pays(None, ln, False)                  # two stages or windows
+    req2, ln2 = lib.plan_rows(np.array([32767] * 3, np.int32), np.array([1] * 3, np.int32))
+    assert not histogram_topk_pays(None, ln2, True)                  # 32768 keys fit one pass
+    req3, ln3 = lib.plan_rows(np.array([65535, 100], np.int32), np.array([1, 4], np.int32))
+    assert not histogram_topk_pays(lib.plan_blocks(req3, 8), ln3, True)  # a prefill block
+    assert histogram_topk_pays(lib.plan_blocks(req3, 1), ln3, True)      # rows scored alone
+    assert not histogram_topk_pays(None, ln[:0], True)               # no rows
+
+
 def test_score_width():
     assert lib.score_width([37, 100]) == 128
     assert lib.score_width([64]) == 64

@@ -458,6 +458,27 @@ def test_step_variants_bit_identical(kw):
         assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
 
 
+def test_step_automatic_histogram_topk():
+    """With a row longer than the one-pass top-k holds at 32 keys per thread
+    and no prefill blocks, the step's automatic choice takes the histogram
+    selection, and it gives the one-pass step's indices and outputs bit for
+    bit (and the oracle's on the long row)."""
+    wl = I.custom(I.decode(), name="long_row", hq=16, hkv=2, topk=256,
+                  prior=(40000, 300, 5000), new=(1, 1, 1), seed=29)
+    inp = _host_inputs(wl)
+    ref = run_step(inp, num_splits=4)
+    outs = [t.clone() for t in (ref.idx, ref.out, ref.out_lse)]
+    step = run_step(inp, num_splits=4, hist=None, topk_chunk=None)
+    _say(f"automatic top-k: histogram {step.use_hist}, chunk {step.topk_chunk}")
+    assert step.use_hist and not step.topk_chunk
+    for a, b in zip(outs, (step.idx, step.out, step.out_lse)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    check_row(step, 0)
+    # with a prefill block the automatic choice keeps the one-pass selection
+    blk = DsaStep(_host_inputs(_small_mixed(seed=29)), block_rows=8, hist=None, topk_chunk=None)
+    assert not blk.use_hist
+
+
 def test_windowed_fp32_tiny():
     from sparse_attention_decode_02_amd import lib
     wl = I.tiny()
