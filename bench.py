@@ -299,10 +299,10 @@ def measure_configs(names, steps, warmup, torch):
         # the step's automatic top-k, or the histogram selection forced on / off
         hist = True if opt == "hist" else False if opt == "onepass" else None
         # the step's automatic choice, or group attention forced on / off
-        group = True if opt == "group" else False if opt == "vector" else None
+        group = True if opt == "group" else False if opt == "split" else None
         wl = I.WORKLOADS[name]()
         print(f"[bench] config {wl.name}{' (histogram top-k)' if hist else ' (one-pass top-k)' if hist is False else ''}"
-              f"{' (group attention)' if group else ' (vector attention)' if group is False else ''}",
+              f"{' (group attention)' if group else ' (split attention only)' if group is False else ''}",
               file=sys.stderr, flush=True)
         inp = I.generate(wl, "cuda")
         step = DsaStep(inp, block_rows=8, fused=None, topk_chunk=0 if hist is not None else None, hist=hist,
@@ -395,16 +395,16 @@ def main(argv=None):
     ap.add_argument("--group-attn", type=int, default=-1,
                     help="1: attention of multi-row score blocks over the union of their "
                          "selections on the matrix cores (dsa_group_attn); 0: every row on the "
-                         "vector kernel; -1 (default): the step's automatic choice")
+                         "split attention kernel; -1 (default): the step's automatic choice")
     ap.add_argument("--graph", action="store_true",
                     help="record the step into a HIP graph once and time its replays")
     ap.add_argument("--cpu-seconds", type=float, default=8.0,
                     help="oracle time budget for cpu_baseline, per core setting (0 = skip)")
     ap.add_argument("--configs",
-                    default="tiny,decode,ragged,mixed,ragged+onepass,mixed+vector,long,long+hist",
+                    default="tiny,decode,ragged,mixed,ragged+onepass,mixed+split,long,long+hist",
                     help="other workloads measured in the same run (comma list, '' = none; "
                          "name+hist / name+onepass: with the histogram top-k forced on / off; "
-                         "name+group / name+vector: group attention forced on / off)")
+                         "name+group / name+split: group attention forced on / off)")
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="instead of the step, run a plain device copy of this many MiB "
                          "(calibrates HBM byte counters)")
@@ -546,7 +546,7 @@ def main(argv=None):
         result["cpu_baseline"] = cpu_baseline(step, args.cpu_seconds, torch)
     this = args.workload + ("+hist" if args.hist > 0 else "+onepass" if args.hist == 0
                             else "+group" if args.group_attn > 0
-                            else "+vector" if args.group_attn == 0 else "")
+                            else "+split" if args.group_attn == 0 else "")
     names = [n for n in args.configs.split(",") if n and n != this]
     if names:
         del step, inp, graph

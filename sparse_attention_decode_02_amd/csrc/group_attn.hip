@@ -9,7 +9,8 @@
 // up to 8 such rows reads each key of the union of their selections once,
 // and for one KV head its 8 rows x 8 query heads = 64 query rows make dense
 // matrix tiles: the contraction is compute-bound, so it runs on the matrix
-// cores (decode rows, with one row per group, stay on the vector kernel).
+// cores (decode rows, with one row per group, stay on the split attention
+// kernel).
 // Row r of the group attends only the keys it selected: the union keeps one
 // mask bit per row, and a key without the row's bit scores -inf for it. The
 // result is dsa_sparse_attn with one split followed by dsa_merge, up to

@@ -86,7 +86,7 @@ class DsaStep:
     of the score blocks of several rows (prefill groups, at most 8 rows) over
     the union of their selections on the matrix cores (dsa_group_attn); rows
     from the first of the trailing one-row blocks on (decode rows) keep the
-    vector kernel. ``group_attn=None`` takes it when the step has such blocks
+    split attention kernel. ``group_attn=None takes it when the step has such blocks
     and none of their rows is longer than 8 x top-k, where a group's rows
     select overlapping keys (measured: a win at 4.25 x top-k, a loss at
     512 x top-k)."""
@@ -206,7 +206,7 @@ class DsaStep:
                                     self.out_lse, prepare=True)]
             g0 = self.group_rows
             if g0 < self.rows:
-                # The decode rows after the groups, on the vector kernel.
+                # The decode rows after the groups, on the split attention kernel.
                 sl = slice(g0, self.rows)
                 splits = lib.sparse_attn_merged_splits(self.rows - g0, wl.hq, wl.hkv, wl.d,
                                                        wl.topk, i.q.dtype)

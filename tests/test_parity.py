@@ -615,7 +615,7 @@ def test_group_attn_matches_oracle(block_rows, topk):
 
 def test_group_attn_step():
     """The step with prefill groups on the matrix cores and the trailing
-    decode rows on the vector kernel: every row against the oracle."""
+    decode rows on the split attention kernel: every row against the oracle."""
     inp = _host_inputs(_prefill_groups_wl(seed=53))
     step = DsaStep(inp, block_rows=8, fused=None, group_attn=True)
     step.scores.view(torch.int32).fill_(CANARY)
@@ -631,7 +631,7 @@ def test_group_attn_step():
 def test_group_attn_automatic_choice():
     """group_attn=None: on where the blocks' rows are short against top-k
     (same bits as group_attn=True), off where they are long (same bits as
-    the vector kernel)."""
+    the split attention kernel)."""
     short = I.custom(I.decode(), name="prefill_groups_short", hq=64, hkv=8, topk=2048,
                      prior=(700, 5000, 60, 0, 3000, 9), new=(37, 9, 8, 3, 1, 1), seed=55)
     inp = _host_inputs(short)
@@ -944,7 +944,8 @@ def test_ragged_full_size():
 
 def test_mixed_group_attn_full_size():
     """The mixed step with its prefill groups on the matrix cores (union of
-    each 8-row group's selections) and its decode rows on the vector kernel:
+    each 8-row group's selections) and its decode rows on the split attention
+    kernel:
     sampled prefill rows, including each request's first and last, and decode
     rows against the oracle."""
     wl = I.mixed()
