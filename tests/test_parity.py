@@ -147,6 +147,11 @@ VARIANTS = [
     ("bf16", 16, 32, 16, 64, 32, 64, 128),
     ("bf16", 64, 16, 1, 128, 64, 128, 100),
     ("bf16", 128, 32, 2, 128, 64, 128, 64),
+    # the matrix-core attention's shape (8 query heads per KV group, d 128)
+    # at other page sizes, KV group counts and top-k not a multiple of 16
+    ("bf16", 16, 8, 1, 128, 64, 128, 100),
+    ("bf16", 128, 64, 8, 128, 64, 128, 48),
+    ("bf16", 32, 16, 2, 128, 32, 64, 257),
     ("f32", 16, 4, 1, 64, 4, 32, 16),
     ("f32", 8, 8, 4, 128, 64, 128, 40),
     ("f32", 64, 16, 2, 64, 17, 64, 64),
