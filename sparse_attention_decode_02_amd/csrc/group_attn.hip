@@ -28,15 +28,18 @@
 //     (global_load_lds, no registers), the copies of the next two tiles in
 //     flight while one is computed; V stays in row order and its B
 //     fragments are read with the transposing ds_read_b64_tr_b16;
-//   * scores: v_mfma_f32_16x16x32_bf16, query rows as A (held in registers),
-//     keys as B; masked keys give -inf; online softmax per query row in
-//     base 2, fp32, against a deferred reference (raised, with a rescale,
-//     only when a score overtakes it by 2^8);
-//   * values: the fp32 probabilities leave the accumulator layout through
-//     LDS and are split exactly into three bf16 terms (p = hi + mid + lo: a
-//     float's 24 significand bits are three bf16 significands), each
-//     multiplied with V on the matrix cores and summed in fp32 -- the
-//     products are exact, so this is the fp32 probability reduction.
+//   * scores, transposed: S^T = K . Q^T on v_mfma_f32_16x16x32_bf16, keys as
+//     A, the query rows (held in registers) as B, so each lane holds one
+//     query row and eight of the tile's keys; masked keys give -inf; online
+//     softmax per query row in base 2, fp32, against a deferred reference
+//     (raised, with a rescale, only when a score overtakes it by 2^8);
+//   * values, transposed: O^T += V^T . P^T, whose B operand is exactly what
+//     the scores left in each lane (the eight keys in the order the V^T
+//     fragments are read), so the probabilities never leave registers; each
+//     is split exactly into three bf16 terms (p = hi + mid + lo: a float's 24
+//     significand bits are three bf16 significands), each multiplied with V
+//     on the matrix cores and summed in fp32 -- the products are exact, so
+//     this is the fp32 probability reduction.
 
 #include "dsa_kernels.h"
 
@@ -63,28 +66,23 @@ constexpr int kWaitVm8 = 8 | (7 << 4) | (15 << 8);
 constexpr int kWaitVm4 = 4 | (7 << 4) | (15 << 8);
 constexpr int kWaitVm0 = 0 | (7 << 4) | (15 << 8);
 constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);  // LDS / scalar only
-constexpr int kPst = kGaTile + 4;  // probability tile row stride (floats)
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr float kLn2 = 0.6931471805599453f;
 constexpr float kGaSlack = 8.0f;  // log2 headroom of the deferred softmax reference
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float v) {
-  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, true));
+// Max / sum over the four lanes l % 16 + 16 g, g < 4 (the lanes holding one
+// query row), every one of them getting the result: two row swaps.
+__device__ __forceinline__ float groups4_max(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
-
-// Max / sum over the 16 lanes of a DPP row (every lane gets the result).
-__device__ __forceinline__ float row16_max(float v) {
-  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
-  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
-  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
-  return fmaxf(v, dpp_f<0x140>(v));  // row_mirror
-}
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_f<0xB1>(v);
-  v += dpp_f<0x4E>(v);
-  v += dpp_f<0x141>(v);
-  return v + dpp_f<0x140>(v);
+__device__ __forceinline__ float groups4_sum(float x) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 __device__ __forceinline__ uint16_t bf16_rne(float f) {
@@ -96,11 +94,12 @@ __device__ __forceinline__ uint16_t bf16_rne(float f) {
 
 // Tile rows are stored unpadded (256 bytes per key) with the 16 16-byte
 // pieces of key j's row permuted: piece p sits in slot p ^ f(j). For K,
-// f(j) = j % 16 spreads the 16 keys of a B-fragment read over all banks; for
-// V (read with the transposing ds_read_b64_tr_b16, four keys x four dims per
-// 16-lane group) f(j) = 2 (j % 4) + 8 ((j / 8) % 2) does the same.
+// f(j) = j % 16 spreads the 16 keys of an A-fragment read over all banks; for
+// V (read with the transposing ds_read_b64_tr_b16: one instruction covers 16
+// consecutive keys, two pieces each) f(j) = 2 (j % 8) puts those 32 pieces
+// two to a slot, the fewest a 512-byte read allows.
 __device__ __forceinline__ int k_slot_xor(int j) { return j & 15; }
-__device__ __forceinline__ int v_slot_xor(int j) { return ((j & 3) << 1) | (((j >> 3) & 1) << 3); }
+__device__ __forceinline__ int v_slot_xor(int j) { return (j & 7) << 1; }
 
 typedef __attribute__((address_space(1))) void ga_gvoid;
 typedef __attribute__((address_space(3))) void ga_lvoid;
@@ -118,13 +117,6 @@ __device__ __forceinline__ void ga_barrier() {
   __builtin_amdgcn_s_barrier();
   __builtin_amdgcn_sched_barrier(0);
   asm volatile("" ::: "memory");
-}
-
-// Orders this wave's LDS writes before its own later LDS reads.
-__device__ __forceinline__ void wave_lds_sync() {
-  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-  __builtin_amdgcn_wave_barrier();
-  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 }
 
 // Exclusive prefix sum over the workgroup (4 waves) in thread order; sh holds
@@ -158,7 +150,7 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
     int page_shift, int max_pages, float scale_log2, uint16_t* __restrict__ out,
     float* __restrict__ out_lse) {
   __shared__ uint32_t bmap[kGaWin / 4];            // the window's byte map: a row bit per position
-  __shared__ uint8_t umask[kGaWin];                // union entry -> its rows' bits
+  __shared__ __attribute__((aligned(4))) uint8_t umask[kGaWin];  // union entry -> its rows' bits
   __shared__ uint32_t urow[kGaWin];                // union entry -> position, then its cache row
   // Tile buffers (K and V of three tiles): [key][128 dims], pieces permuted
   // per key. Separate arrays, each named where it is used, so that the
@@ -167,7 +159,6 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
   __shared__ __attribute__((aligned(16))) uint16_t kbuf0[kGaTile * kGaD], vbuf0[kGaTile * kGaD];
   __shared__ __attribute__((aligned(16))) uint16_t kbuf1[kGaTile * kGaD], vbuf1[kGaTile * kGaD];
   __shared__ __attribute__((aligned(16))) uint16_t kbuf2[kGaTile * kGaD], vbuf2[kGaTile * kGaD];
-  __shared__ __attribute__((aligned(16))) float p_lds[4][16 * kPst];
   __shared__ int cursor[kGaRows];
   __shared__ int nextpos[kGaRows];
   __shared__ uint32_t scan_sh[2][4];
@@ -186,7 +177,7 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
   const uint16_t* kgroup = kc + (size_t)j * kGaD;
   const uint16_t* vgroup = vc + (size_t)j * kGaD;
 
-  // The wave's query rows as MFMA A fragments: lane l holds query row l % 16
+  // The wave's query rows as MFMA B fragments: lane l holds query row l % 16
   // (group row 2w + (l % 16) / 8, head j * 8 + l % 8), dims kk * 32 +
   // (l / 16) * 8 .. + 8 of step kk. Rows past the group are zero.
   const int qrow = lane & 15, kgrp = lane >> 4;
@@ -203,16 +194,11 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
         qa[kk] = bf16x8_t{};
     }
   }
-  // Accumulator rows of this lane: (l / 16) * 4 + i, i < 4, all of group row
-  // 2w + (l >= 32).
-  const int my_tr = 2 * wave + (lane >> 5);
-  float m[4], lsum[4];
+  // This lane's query row (its scores, reference, running sum and the
+  // column of O^T it accumulates: dims nt * 16 + (l / 16) * 4 + i).
+  const int my_tr = 2 * wave + (qrow >> 3);
+  float m = -INFINITY, lsum = 0.0f;
   f32x4_t o[kGaD / 16];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    m[i] = -INFINITY;
-    lsum[i] = 0.0f;
-  }
 #pragma unroll
   for (int nt = 0; nt < kGaD / 16; ++nt) o[nt] = f32x4_t{};
 
@@ -344,7 +330,8 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
       }
       ga_barrier();  // every wave's copies of tile t are in LDS
-      // Scores: 16 query rows x 32 keys.
+      // Scores S^T: keys n * 16 + 4 (l / 16) + i of the tile (i < 4) for
+      // query row l % 16.
       f32x4_t s[2];
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
@@ -354,93 +341,77 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
           const int key = n * 16 + qrow;
           const bf16x8_t kb = *reinterpret_cast<const bf16x8_t*>(
               k_lds + key * kGaD + 8 * ((kk * 4 + kgrp) ^ k_slot_xor(key)));
-          s[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[kk], kb, s[n], 0, 0, 0);
+          s[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qa[kk], s[n], 0, 0, 0);
         }
       }
-      // Mask: key n * 16 + l % 16 of the tile, for group row my_tr.
-      bool ok[2];
+      // Mask: the four union entries e0 + n * 16 + 4 (l / 16) .. + 3 in one
+      // word of the byte map, bit my_tr of each.
+      float x[2][4];
+      bool over = false;
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
-        const int e = e0 + n * 16 + qrow;
-        ok[n] = e < (int)n_u && ((umask[min(e, kGaWin - 1)] >> my_tr) & 1u);
+        const int eb = e0 + n * 16 + 4 * kgrp;
+        const uint32_t mw = *reinterpret_cast<const uint32_t*>(umask + eb) >> my_tr;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = eb + i < (int)n_u && ((mw >> (8 * i)) & 1u);
+          x[n][i] = ok ? s[n][i] * scale_log2 : -INFINITY;
+          over |= x[n][i] > m + kGaSlack;
+        }
       }
       // Online softmax against a deferred reference: a row's m is raised to
       // its running max (and its sum and outputs rescaled) only when a score
       // overtakes it by more than 2^kGaSlack, so most tiles skip the
       // rescale; o and the sum share the reference, so the normalized
       // result is the same and every probability stays <= 2^kGaSlack.
-      bool over = false;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float x = fmaxf(ok[0] ? s[0][i] * scale_log2 : -INFINITY,
-                              ok[1] ? s[1][i] * scale_log2 : -INFINITY);
-        over |= x > m[i] + kGaSlack;
-      }
       if (__ballot(over) != 0) {
+        float xm = fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3]));
+        xm = fmaxf(xm, fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+        const float mt = groups4_max(xm);
+        const bool up = mt > m + kGaSlack;
+        // m = -inf (no selected key yet): alpha = 0 clears what is zero.
+        const float alpha = up ? __builtin_amdgcn_exp2f(m - mt) : 1.0f;
+        lsum *= alpha;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const float x = fmaxf(ok[0] ? s[0][i] * scale_log2 : -INFINITY,
-                                ok[1] ? s[1][i] * scale_log2 : -INFINITY);
-          const float mt = row16_max(x);
-          const bool up = mt > m[i] + kGaSlack;
-          // m = -inf (no selected key yet): alpha = 0 clears what is zero.
-          const float alpha = up ? __builtin_amdgcn_exp2f(m[i] - mt) : 1.0f;
-          lsum[i] *= alpha;
-#pragma unroll
-          for (int nt = 0; nt < kGaD / 16; ++nt) o[nt][i] *= alpha;
-          m[i] = up ? mt : m[i];
-        }
+        for (int nt = 0; nt < kGaD / 16; ++nt) o[nt] *= alpha;
+        m = up ? mt : m;
       }
-      float pv[2][4];
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        // A masked key has probability 0 whatever the reference (before a
-        // row's first selected key m is still -inf).
-        pv[0][i] = ok[0] ? __builtin_amdgcn_exp2f(s[0][i] * scale_log2 - m[i]) : 0.0f;
-        pv[1][i] = ok[1] ? __builtin_amdgcn_exp2f(s[1][i] * scale_log2 - m[i]) : 0.0f;
-        lsum[i] += pv[0][i] + pv[1][i];
-      }
-      // Probabilities to the A layout through LDS (row l % 16, keys
-      // (l / 16) * 8 .. + 8), split into three exact bf16 terms.
-      float* pw = p_lds[wave];
+      // Probabilities (a masked key has 0 whatever the reference: before a
+      // row's first selected key m is still -inf), split into three exact
+      // bf16 terms: the B operands of O^T += V^T . P^T, k index 8 (l / 16) +
+      // 4 n + i holding key n * 16 + 4 (l / 16) + i.
+      uint16_t hb[8], mb[8], lb[8];
+      float ps = 0.0f;
 #pragma unroll
       for (int n = 0; n < 2; ++n)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pw[(kgrp * 4 + i) * kPst + n * 16 + qrow] = pv[n][i];
-      wave_lds_sync();
-      bf16x8_t ph, pm, pl;
-      {
-        const float4 x0 = *reinterpret_cast<const float4*>(pw + qrow * kPst + kgrp * 8);
-        const float4 x1 = *reinterpret_cast<const float4*>(pw + qrow * kPst + kgrp * 8 + 4);
-        const float xs[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-        uint16_t hb[8], mb[8], lb[8];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const uint32_t u0 = __float_as_uint(xs[e]);
-          const float h = __uint_as_float(u0 & 0xFFFF0000u);
-          const float r1 = xs[e] - h;  // exact
-          const float mid = __uint_as_float(__float_as_uint(r1) & 0xFFFF0000u);
-          const float r2 = r1 - mid;   // exact
-          hb[e] = (uint16_t)(u0 >> 16);
-          mb[e] = (uint16_t)(__float_as_uint(mid) >> 16);
-          lb[e] = (uint16_t)(__float_as_uint(r2) >> 16);  // exact: at most 8 bits left
+        for (int i = 0; i < 4; ++i) {
+          const float p = x[n][i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[n][i] - m);
+          ps += p;
+          const uint32_t u0 = __float_as_uint(p);
+          const float r1 = p - __uint_as_float(u0 & 0xFFFF0000u);  // exact
+          const uint32_t u1 = __float_as_uint(r1);
+          const float r2 = r1 - __uint_as_float(u1 & 0xFFFF0000u);  // exact, <= 8 bits left
+          hb[4 * n + i] = (uint16_t)(u0 >> 16);
+          mb[4 * n + i] = (uint16_t)(u1 >> 16);
+          lb[4 * n + i] = (uint16_t)(__float_as_uint(r2) >> 16);
         }
-        ph = __builtin_bit_cast(bf16x8_t, hb);
-        pm = __builtin_bit_cast(bf16x8_t, mb);
-        pl = __builtin_bit_cast(bf16x8_t, lb);
-      }
-      // Values: O[16 x 128] += P[16 x 32] . V[32 x 128], three terms. The B
-      // fragment (dim nt * 16 + l % 16, keys (l / 16) * 8 .. + 8) comes from
+      lsum += ps;
+      const bf16x8_t ph = __builtin_bit_cast(bf16x8_t, hb);
+      const bf16x8_t pm = __builtin_bit_cast(bf16x8_t, mb);
+      const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, lb);
+      // Values: O^T[128 x 16] += V^T[128 x 32] . P^T[32 x 16], three terms.
+      // The A fragment (dim nt * 16 + l % 16, the same eight keys) comes from
       // two transposing reads: lane j of a 16-lane group addresses the four
-      // dims nt * 16 + 4 (j % 4) .. + 4 of key (l / 16) * 8 + j / 4 (+ 4), and
-      // lane m receives dim nt * 16 + m of the four keys.
+      // dims nt * 16 + 4 (j % 4) .. + 4 of key hh * 16 + 4 (l / 16) + j / 4,
+      // and lane m receives dim nt * 16 + m of those four keys.
       const int jq = qrow & 3, jk = qrow >> 2;
 #pragma unroll
       for (int nt = 0; nt < kGaD / 16; ++nt) {
         bf16x4_t vh[2];
 #pragma unroll
         for (int hh = 0; hh < 2; ++hh) {
-          const int key = kgrp * 8 + hh * 4 + jk;
+          const int key = hh * 16 + kgrp * 4 + jk;
           const int d = nt * 16 + 4 * jq;
           const uint16_t* src = v_lds + key * kGaD + 8 * ((d >> 3) ^ v_slot_xor(key)) + (d & 7);
           vh[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
@@ -448,9 +419,9 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
         }
         const bf16x8_t vb = {vh[0][0], vh[0][1], vh[0][2], vh[0][3],
                              vh[1][0], vh[1][1], vh[1][2], vh[1][3]};
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ph, vb, o[nt], 0, 0, 0);
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pm, vb, o[nt], 0, 0, 0);
-        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(pl, vb, o[nt], 0, 0, 0);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, ph, o[nt], 0, 0, 0);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pm, o[nt], 0, 0, 0);
+        o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pl, o[nt], 0, 0, 0);
       }
       // Every wave's reads of this tile's buffers are done (their MFMAs have
       // issued) before any wave copies a later tile into them.
@@ -472,20 +443,22 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
   }
 
   // ---- the rows' outputs ----
+  // The row's sum over the four lanes holding it (every one of them joins).
+  const float l = groups4_sum(lsum);
   if (my_tr < nrows) {
     const int r = first + my_tr;
+    const bool any = l > 0.0f;
+    const float inv = any ? 1.0f / l : 0.0f;
+    const int h = j * kGaG + (qrow & 7);
+    uint16_t* orow = out + ((size_t)r * hq + h) * kGaD + 4 * kgrp;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float l = row16_sum(lsum[i]);
-      const bool any = l > 0.0f;
-      const float inv = any ? 1.0f / l : 0.0f;
-      const int h = j * kGaG + ((kgrp * 4 + i) & 7);
-      uint16_t* orow = out + ((size_t)r * hq + h) * kGaD;
-#pragma unroll
-      for (int nt = 0; nt < kGaD / 16; ++nt) orow[nt * 16 + qrow] = bf16_rne(o[nt][i] * inv);
-      if (out_lse && qrow == 0)
-        out_lse[(size_t)r * hq + h] = any ? (m[i] + __log2f(l)) * kLn2 : -INFINITY;
+    for (int nt = 0; nt < kGaD / 16; ++nt) {
+      const uint32_t lo = bf16_rne(o[nt][0] * inv) | ((uint32_t)bf16_rne(o[nt][1] * inv) << 16);
+      const uint32_t hi = bf16_rne(o[nt][2] * inv) | ((uint32_t)bf16_rne(o[nt][3] * inv) << 16);
+      *reinterpret_cast<uint2*>(orow + nt * 16) = make_uint2(lo, hi);
     }
+    if (out_lse && kgrp == 0)
+      out_lse[(size_t)r * hq + h] = any ? (m + __log2f(l)) * kLn2 : -INFINITY;
   }
 }
 
