@@ -344,6 +344,26 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
           s[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qa[kk], s[n], 0, 0, 0);
         }
       }
+      // V^T fragments of the value product (below), read now so that their
+      // latency hides behind the softmax: the A fragment (dim nt * 16 + l %
+      // 16, the eight keys of this lane's probabilities) comes from two
+      // transposing reads: lane j of a 16-lane group addresses the four dims
+      // nt * 16 + 4 (j % 4) .. + 4 of key hh * 16 + 4 (l / 16) + j / 4, and
+      // lane m receives dim nt * 16 + m of those four keys.
+      bf16x4_t vh[kGaD / 16][2];
+      {
+        const int jq = qrow & 3, jk = qrow >> 2;
+#pragma unroll
+        for (int nt = 0; nt < kGaD / 16; ++nt)
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int key = hh * 16 + kgrp * 4 + jk;
+            const int d = nt * 16 + 4 * jq;
+            const uint16_t* src = v_lds + key * kGaD + 8 * ((d >> 3) ^ v_slot_xor(key)) + (d & 7);
+            vh[nt][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+                (ga_lds_bf16x4*)(__attribute__((address_space(3))) uint16_t*)src);
+          }
+      }
       // Mask: the four union entries e0 + n * 16 + 4 (l / 16) .. + 3 in one
       // word of the byte map, bit my_tr of each.
       float x[2][4];
@@ -401,24 +421,10 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
       const bf16x8_t pm = __builtin_bit_cast(bf16x8_t, mb);
       const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, lb);
       // Values: O^T[128 x 16] += V^T[128 x 32] . P^T[32 x 16], three terms.
-      // The A fragment (dim nt * 16 + l % 16, the same eight keys) comes from
-      // two transposing reads: lane j of a 16-lane group addresses the four
-      // dims nt * 16 + 4 (j % 4) .. + 4 of key hh * 16 + 4 (l / 16) + j / 4,
-      // and lane m receives dim nt * 16 + m of those four keys.
-      const int jq = qrow & 3, jk = qrow >> 2;
 #pragma unroll
       for (int nt = 0; nt < kGaD / 16; ++nt) {
-        bf16x4_t vh[2];
-#pragma unroll
-        for (int hh = 0; hh < 2; ++hh) {
-          const int key = hh * 16 + kgrp * 4 + jk;
-          const int d = nt * 16 + 4 * jq;
-          const uint16_t* src = v_lds + key * kGaD + 8 * ((d >> 3) ^ v_slot_xor(key)) + (d & 7);
-          vh[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-              (ga_lds_bf16x4*)(__attribute__((address_space(3))) uint16_t*)src);
-        }
-        const bf16x8_t vb = {vh[0][0], vh[0][1], vh[0][2], vh[0][3],
-                             vh[1][0], vh[1][1], vh[1][2], vh[1][3]};
+        const bf16x8_t vb = {vh[nt][0][0], vh[nt][0][1], vh[nt][0][2], vh[nt][0][3],
+                             vh[nt][1][0], vh[nt][1][1], vh[nt][1][2], vh[nt][1][3]};
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, ph, o[nt], 0, 0, 0);
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pm, o[nt], 0, 0, 0);
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pl, o[nt], 0, 0, 0);
