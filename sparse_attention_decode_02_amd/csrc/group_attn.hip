@@ -24,10 +24,13 @@
 //     then compacted in position order into (offset, mask) entries;
 //   * each entry's cache row is resolved through the block table once per
 //     window; tiles of 32 union keys: the keys' K and V rows for the KV head
-//     are copied straight from global memory into one of three LDS buffers
-//     (global_load_lds, no registers), the copies of the next two tiles in
-//     flight while one is computed; V stays in row order and its B
-//     fragments are read with the transposing ds_read_b64_tr_b16;
+//     are copied straight from global memory into one of two LDS buffers
+//     (global_load_lds, no registers), the copies of the next tile in flight
+//     while one is computed; V stays in row order and its A fragments are
+//     read with the transposing ds_read_b64_tr_b16;
+//   * 45 KB of LDS and at most 168 VGPRs a lane let three workgroups share a
+//     compute unit, which hides more of each wave's barrier and load waits
+//     than a deeper copy pipeline (three buffers, two workgroups) did;
 //   * scores, transposed: S^T = K . Q^T on v_mfma_f32_16x16x32_bf16, keys as
 //     A, the query rows (held in registers) as B, so each lane holds one
 //     query row and eight of the tile's keys; masked keys give -inf; online
@@ -58,11 +61,9 @@ constexpr int kGaTile = 32;      // union keys per tile
 constexpr int kGaRows = 8;       // rows per group, at most
 constexpr int kGaD = 128;        // head dim
 constexpr int kGaG = 8;          // query heads per KV head
-constexpr int kGaStages = 3;     // LDS tile buffers: two tiles' loads in flight, one computed
 // s_waitcnt immediates (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt
-// 6:4, lgkmcnt 11:8): wait until at most 8, 4 or 0 vector memory
-// instructions are outstanding, nothing else.
-constexpr int kWaitVm8 = 8 | (7 << 4) | (15 << 8);
+// 6:4, lgkmcnt 11:8): wait until at most 4 or 0 vector memory instructions
+// are outstanding, nothing else.
 constexpr int kWaitVm4 = 4 | (7 << 4) | (15 << 8);
 constexpr int kWaitVm0 = 0 | (7 << 4) | (15 << 8);
 constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);  // LDS / scalar only
@@ -143,7 +144,8 @@ __device__ __forceinline__ uint32_t ga_block_scan(uint32_t v, uint32_t* sh, uint
 
 }  // namespace
 
-__global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
+// Three workgroups per compute unit: at most 168 VGPRs a lane.
+__global__ __launch_bounds__(kGaThreads, 3) void group_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ row_req,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ groups, int hkv, int k,
@@ -152,13 +154,12 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
   __shared__ uint32_t bmap[kGaWin / 4];            // the window's byte map: a row bit per position
   __shared__ __attribute__((aligned(4))) uint8_t umask[kGaWin];  // union entry -> its rows' bits
   __shared__ uint32_t urow[kGaWin];                // union entry -> position, then its cache row
-  // Tile buffers (K and V of three tiles): [key][128 dims], pieces permuted
+  // Tile buffers (K and V of two tiles): [key][128 dims], pieces permuted
   // per key. Separate arrays, each named where it is used, so that the
-  // compiler can tell a tile's reads from the copies into the other buffers
+  // compiler can tell a tile's reads from the copies into the other buffer
   // and waits only for the copies it reads.
   __shared__ __attribute__((aligned(16))) uint16_t kbuf0[kGaTile * kGaD], vbuf0[kGaTile * kGaD];
   __shared__ __attribute__((aligned(16))) uint16_t kbuf1[kGaTile * kGaD], vbuf1[kGaTile * kGaD];
-  __shared__ __attribute__((aligned(16))) uint16_t kbuf2[kGaTile * kGaD], vbuf2[kGaTile * kGaD];
   __shared__ int cursor[kGaRows];
   __shared__ int nextpos[kGaRows];
   __shared__ uint32_t scan_sh[2][4];
@@ -310,21 +311,18 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
     __syncthreads();
 
     // ---- tiles of the window's union ----
-    // Tile t is computed from buffer t % 3 while the loads of tiles t + 1
-    // and t + 2 are in flight; a wave's own loads of tile t are complete
-    // when at most the later tiles' instructions (4 per tile) are
-    // outstanding, and a barrier then covers every wave's. A second barrier
-    // closes each tile before its buffer is loaded again.
+    // Tile t is computed from buffer t % 2 while the copies of tile t + 1
+    // are in flight; a wave's own copies of tile t are complete when at most
+    // the next tile's four instructions are outstanding, and a barrier then
+    // covers every wave's. A second barrier closes each tile before its
+    // buffer is loaded again.
     const int ntiles = ((int)n_u + kGaTile - 1) / kGaTile;
-    // One tile: wait for its copies (and let those of the next two fly),
-    // compute it from (k_lds, v_lds), then close it before its buffers are
-    // reused.
+    // One tile: start the next tile's copies, wait for this one's, compute
+    // it from (k_lds, v_lds), then close it before its buffers are reused.
     auto tile = [&](int t, const uint16_t* k_lds, const uint16_t* v_lds, auto&& issue_ahead) {
       const int e0 = t * kGaTile;
-      if (t + 2 < ntiles) {
+      if (t + 1 < ntiles) {
         issue_ahead();
-        __builtin_amdgcn_s_waitcnt(kWaitVm8);
-      } else if (t + 1 < ntiles) {
         __builtin_amdgcn_s_waitcnt(kWaitVm4);
       } else {
         __builtin_amdgcn_s_waitcnt(kWaitVm0);
@@ -343,26 +341,6 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
               k_lds + key * kGaD + 8 * ((kk * 4 + kgrp) ^ k_slot_xor(key)));
           s[n] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kb, qa[kk], s[n], 0, 0, 0);
         }
-      }
-      // V^T fragments of the value product (below), read now so that their
-      // latency hides behind the softmax: the A fragment (dim nt * 16 + l %
-      // 16, the eight keys of this lane's probabilities) comes from two
-      // transposing reads: lane j of a 16-lane group addresses the four dims
-      // nt * 16 + 4 (j % 4) .. + 4 of key hh * 16 + 4 (l / 16) + j / 4, and
-      // lane m receives dim nt * 16 + m of those four keys.
-      bf16x4_t vh[kGaD / 16][2];
-      {
-        const int jq = qrow & 3, jk = qrow >> 2;
-#pragma unroll
-        for (int nt = 0; nt < kGaD / 16; ++nt)
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int key = hh * 16 + kgrp * 4 + jk;
-            const int d = nt * 16 + 4 * jq;
-            const uint16_t* src = v_lds + key * kGaD + 8 * ((d >> 3) ^ v_slot_xor(key)) + (d & 7);
-            vh[nt][hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
-                (ga_lds_bf16x4*)(__attribute__((address_space(3))) uint16_t*)src);
-          }
       }
       // Mask: the four union entries e0 + n * 16 + 4 (l / 16) .. + 3 in one
       // word of the byte map, bit my_tr of each.
@@ -421,10 +399,25 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
       const bf16x8_t pm = __builtin_bit_cast(bf16x8_t, mb);
       const bf16x8_t pl = __builtin_bit_cast(bf16x8_t, lb);
       // Values: O^T[128 x 16] += V^T[128 x 32] . P^T[32 x 16], three terms.
+      // The A fragment (dim nt * 16 + l % 16, the eight keys of this lane's
+      // probabilities) comes from two transposing reads: lane j of a 16-lane
+      // group addresses the four dims nt * 16 + 4 (j % 4) .. + 4 of key
+      // hh * 16 + 4 (l / 16) + j / 4, and lane m receives dim nt * 16 + m of
+      // those four keys.
+      const int jq = qrow & 3, jk = qrow >> 2;
 #pragma unroll
       for (int nt = 0; nt < kGaD / 16; ++nt) {
-        const bf16x8_t vb = {vh[nt][0][0], vh[nt][0][1], vh[nt][0][2], vh[nt][0][3],
-                             vh[nt][1][0], vh[nt][1][1], vh[nt][1][2], vh[nt][1][3]};
+        bf16x4_t vh[2];
+#pragma unroll
+        for (int hh = 0; hh < 2; ++hh) {
+          const int key = hh * 16 + kgrp * 4 + jk;
+          const int d = nt * 16 + 4 * jq;
+          const uint16_t* src = v_lds + key * kGaD + 8 * ((d >> 3) ^ v_slot_xor(key)) + (d & 7);
+          vh[hh] = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+              (ga_lds_bf16x4*)(__attribute__((address_space(3))) uint16_t*)src);
+        }
+        const bf16x8_t vb = {vh[0][0], vh[0][1], vh[0][2], vh[0][3],
+                             vh[1][0], vh[1][1], vh[1][2], vh[1][3]};
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, ph, o[nt], 0, 0, 0);
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pm, o[nt], 0, 0, 0);
         o[nt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vb, pl, o[nt], 0, 0, 0);
@@ -435,13 +428,10 @@ __global__ __launch_bounds__(kGaThreads, 2) void group_attn_kernel(
       ga_barrier();
     };
     issue_tile(0, kbuf0, vbuf0, (int)n_u);
-    if (1 < ntiles) issue_tile(1, kbuf1, vbuf1, (int)n_u);
-    for (int t = 0; t < ntiles; t += 3) {
-      tile(t, kbuf0, vbuf0, [&] { issue_tile(t + 2, kbuf2, vbuf2, (int)n_u); });
+    for (int t = 0; t < ntiles; t += 2) {
+      tile(t, kbuf0, vbuf0, [&] { issue_tile(t + 1, kbuf1, vbuf1, (int)n_u); });
       if (t + 1 >= ntiles) break;
-      tile(t + 1, kbuf1, vbuf1, [&] { issue_tile(t + 3, kbuf0, vbuf0, (int)n_u); });
-      if (t + 2 >= ntiles) break;
-      tile(t + 2, kbuf2, vbuf2, [&] { issue_tile(t + 4, kbuf1, vbuf1, (int)n_u); });
+      tile(t + 1, kbuf1, vbuf1, [&] { issue_tile(t + 2, kbuf0, vbuf0, (int)n_u); });
     }
     // The next window rebuilds the byte map and the union list after this
     // barrier (every read of them is done).
