@@ -28,9 +28,10 @@
 //     (global_load_lds, no registers), the copies of the next tile in flight
 //     while one is computed; V stays in row order and its A fragments are
 //     read with the transposing ds_read_b64_tr_b16;
-//   * 45 KB of LDS and at most 168 VGPRs a lane let three workgroups share a
-//     compute unit, which hides more of each wave's barrier and load waits
-//     than a deeper copy pipeline (three buffers, two workgroups) did;
+//   * 39 KB of LDS (windows of 1024 positions, two tile buffers) and at most
+//     128 VGPRs a lane let four workgroups share a compute unit, which hides
+//     more of each wave's barrier and load waits than a deeper copy
+//     pipeline (three buffers, two workgroups) did;
 //   * scores, transposed: S^T = K . Q^T on v_mfma_f32_16x16x32_bf16, keys as
 //     A, the query rows (held in registers) as B, so each lane holds one
 //     query row and eight of the tile's keys; masked keys give -inf; online
@@ -54,7 +55,7 @@ typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kGaThreads = 256;  // 4 waves
-constexpr int kGaWin = 2048;     // positions per union window
+constexpr int kGaWin = 1024;     // positions per union window
 constexpr int kWpt = kGaWin / 4 / kGaThreads;  // byte-map words per thread in the compaction
 static_assert(kWpt >= 1 && kWpt * 4 * kGaThreads == kGaWin, "the compaction covers the window exactly");
 constexpr int kGaTile = 32;      // union keys per tile
@@ -144,8 +145,8 @@ __device__ __forceinline__ uint32_t ga_block_scan(uint32_t v, uint32_t* sh, uint
 
 }  // namespace
 
-// Three workgroups per compute unit: at most 168 VGPRs a lane.
-__global__ __launch_bounds__(kGaThreads, 3) void group_attn_kernel(
+// Four workgroups per compute unit: at most 128 VGPRs a lane.
+__global__ __launch_bounds__(kGaThreads, 4) void group_attn_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ kc, const uint16_t* __restrict__ vc,
     const int32_t* __restrict__ bt, const int32_t* __restrict__ row_req,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ groups, int hkv, int k,
