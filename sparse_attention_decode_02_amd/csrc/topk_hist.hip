@@ -332,34 +332,67 @@ __global__ __launch_bounds__(kThreads) void topk_hist_kernel(const float* __rest
 
 // Counts of each row's scores over the top 12 bits of their order keys,
 // added to hist[r] (which the caller has cleared). Workgroup (r, g) of the G
-// per row counts the row's chunks g, g + G, ... in LDS, then adds its
-// non-empty bins with one global atomic each.
+// per row counts the row's chunks g, g + G, ... of kHistChunk positions; a
+// thread loads its 32 consecutive scores of a chunk (eight 16-byte loads in
+// flight) before counting them. A row's scores crowd into a few bins, and
+// LDS atomics of one instruction to one address serialize, so lane l counts
+// into copy l % kHistCopies of the histogram (16-bit counters, two bins a
+// word); the copies are summed when the bins join the row's, one global
+// atomic per non-empty bin. A copy takes 64 threads x 32 keys per chunk, so
+// a workgroup counts at most kHistMaxIters chunks (the launch sets G).
 constexpr int kHistThreads = 256;
-constexpr int kHistChunk = 8192;
-constexpr int kHistGroups = 8;  // workgroups per row, at most
+constexpr int kHistVPT = 32;
+constexpr int kHistChunk = kHistThreads * kHistVPT;  // 8192
+constexpr int kHistCopies = 4;
+constexpr int kHistMaxIters = 65535 / (kHistThreads / kHistCopies * kHistVPT);  // 31
+constexpr int kHistWords = kHistBins / 2;  // per copy
 
 __global__ __launch_bounds__(kHistThreads) void score_hist_kernel(const float* __restrict__ scores,
                                                                  const int32_t* __restrict__ row_len,
                                                                  int width, int groups,
                                                                  uint32_t* __restrict__ hist) {
-  __shared__ uint32_t h[kHistBins];
+  __shared__ uint32_t h[kHistCopies * kHistWords];
   const int r = blockIdx.x / groups;
   const int g = blockIdx.x - r * groups;
   const int L = row_len[r];
   if (g * kHistChunk >= L) return;  // uniform over the workgroup
-  for (int i = threadIdx.x; i < kHistBins; i += kHistThreads) h[i] = 0u;
+  for (int i = threadIdx.x; i < kHistCopies * kHistWords; i += kHistThreads) h[i] = 0u;
   __syncthreads();
   const float* row = scores + (size_t)r * width;
+  uint32_t* hc = h + (threadIdx.x % kHistCopies) * kHistWords;
+  auto count = [&](float x) {
+    const uint32_t bin = order_key(x) >> kHistShift;
+    atomicAdd(&hc[bin >> 1], 1u << ((bin & 1u) << 4));
+  };
   for (int c0 = g * kHistChunk; c0 < L; c0 += groups * kHistChunk) {
-    const int end = min(L, c0 + kHistChunk);
-    for (int i = c0 + (int)threadIdx.x; i < end; i += kHistThreads)
-      atomicAdd(&h[order_key(row[i]) >> kHistShift], 1u);
+    const int p = c0 + (int)threadIdx.x * kHistVPT;
+    if (p + kHistVPT <= L) {
+      float4 v[kHistVPT / 4];
+#pragma unroll
+      for (int u = 0; u < kHistVPT / 4; ++u) v[u] = *reinterpret_cast<const float4*>(row + p + 4 * u);
+#pragma unroll
+      for (int u = 0; u < kHistVPT / 4; ++u) {
+        count(v[u].x);
+        count(v[u].y);
+        count(v[u].z);
+        count(v[u].w);
+      }
+    } else {
+      for (int j = p; j < L; ++j) count(row[j]);
+    }
   }
   __syncthreads();
   uint32_t* hr = hist + (size_t)r * kHistBins;
-  for (int i = threadIdx.x; i < kHistBins; i += kHistThreads) {
-    const uint32_t n = h[i];
-    if (n) atomicAdd(&hr[i], n);
+  for (int i = threadIdx.x; i < kHistWords; i += kHistThreads) {
+    uint32_t lo = 0u, hi = 0u;
+#pragma unroll
+    for (int c = 0; c < kHistCopies; ++c) {
+      const uint32_t n = h[c * kHistWords + i];
+      lo += n & 0xFFFFu;
+      hi += n >> 16;
+    }
+    if (lo) atomicAdd(&hr[2 * i], lo);
+    if (hi) atomicAdd(&hr[2 * i + 1], hi);
   }
 }
 
@@ -379,8 +412,17 @@ hipError_t launch_score_hist(const float* scores, const int32_t* row_len, int ro
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
+  // Workgroups per row: about four per compute unit over the batch, at most
+  // one per chunk, and enough that none counts more than kHistMaxIters
+  // chunks (its 16-bit counters).
+  int cus = device_cus();
+  if (cus <= 0) cus = 256;
   const int chunks = (width + kHistChunk - 1) / kHistChunk;
-  const int groups = chunks < kHistGroups ? chunks : kHistGroups;
+  const long long want = (4LL * cus + rows - 1) / rows;
+  int groups = (int)(want < chunks ? want : chunks);
+  const int least = (chunks + kHistMaxIters - 1) / kHistMaxIters;
+  if (groups < least) groups = least;
+  if (groups < 1) groups = 1;
   hipLaunchKernelGGL(score_hist_kernel, dim3((unsigned)((long long)rows * groups)),
                      dim3(kHistThreads), 0, stream, scores, row_len, width, groups, hist);
   return hipGetLastError();

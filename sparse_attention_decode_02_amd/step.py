@@ -39,17 +39,27 @@ ONE_PASS_RESIDENT_KEYS = 32768
 
 def histogram_topk_pays(blocks, row_len, one_pass):
     """The step's automatic choice of the histogram top-k (dsa_indexer_scores_hist
-    + dsa_topk_hist): the selection runs in one pass (no score windows, no
-    two stages), no score block holds more than one row (the block indexer
-    would need a separate counting pass over the written scores), and some
-    row is longer than ``ONE_PASS_RESIDENT_KEYS``. Measured: ragged batch 64
-    x 1..65536 193 -> 179 us; it loses at 32768 keys (+0.7 us), on a mixed
-    step with prefill blocks (+170 us) and at decode batch 8 (+2 us)."""
-    if not one_pass or len(row_len) == 0:
+    + dsa_topk_hist), for a step without score windows or a forced two-stage
+    selection. ``one_pass``: the library would otherwise select in one pass.
+
+    With score blocks of several rows (prefill), the block indexer does not
+    count as it scores, so a separate pass counts the written scores; that
+    pays only against the two-stage selection of long prefill rows: some
+    row of such a block is longer than 2 x ``ONE_PASS_RESIDENT_KEYS`` (the
+    one-pass kernel's limit at 64 keys per thread). Measured: 2048 prefill
+    rows at 1M context 32.0 -> 31.3 ms; a mixed step whose prefill rows are
+    8.5K keys long loses (1642 -> 1714 us).
+    Otherwise: the selection runs in one pass and some row is longer than
+    ``ONE_PASS_RESIDENT_KEYS``. Measured: ragged batch 64 x 1..65536 193 ->
+    179 us; it loses at 32768 keys (+0.7 us), at decode batch 8 (+2 us) and
+    against the two-stage selection of 64 rows at 200K (785 vs 788 us)."""
+    if len(row_len) == 0:
         return False
-    if blocks is not None and any(int(n) > 1 for _, n in blocks):
-        return False
-    return int(row_len.max()) > ONE_PASS_RESIDENT_KEYS
+    multi = [] if blocks is None else [(int(b0), int(n)) for b0, n in blocks if int(n) > 1]
+    if multi:
+        longest = max(int(row_len[b0:b0 + n].max()) for b0, n in multi)
+        return longest > 2 * ONE_PASS_RESIDENT_KEYS
+    return one_pass and int(row_len.max()) > ONE_PASS_RESIDENT_KEYS
 
 
 class _Seq:
@@ -125,15 +135,16 @@ class DsaStep:
             self.window_rows = min(self.rows, lib.select_window_rows(self.width, score_buffer_bytes))
         if hist and (score_buffer_bytes is not None or topk_chunk):
             raise ValueError("the histogram top-k does not combine with score windows or two stages")
-        if hist:
-            topk_chunk = 0
-        if topk_chunk is None:
+        suggested = topk_chunk
+        if suggested is None:
             # The suggestion for a window's rows, at the batch's fill.
             window_keys = self.total_keys * self.window_rows // max(1, self.rows)
-            topk_chunk = lib.topk_chunk_suggest(self.window_rows, self.width, wl.topk, window_keys)
+            suggested = lib.topk_chunk_suggest(self.window_rows, self.width, wl.topk, window_keys)
         if hist is None:
-            hist = histogram_topk_pays(self.blocks_host, ln,
-                                       score_buffer_bytes is None and not topk_chunk)
+            # Not with score windows or a two-stage selection the caller asked for.
+            hist = (score_buffer_bytes is None and not topk_chunk
+                    and histogram_topk_pays(self.blocks_host, ln, not suggested))
+        topk_chunk = 0 if hist else suggested
         self.use_hist = hist
         self.topk_chunk = topk_chunk
         self.windowed = score_buffer_bytes is not None

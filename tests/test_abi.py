@@ -87,7 +87,9 @@ def test_group_attention_automatic_choice():
 def test_histogram_topk_automatic_choice():
     """The step takes the histogram top-k when it selects in one pass, has no
     multi-row score blocks and some row is longer than the one-pass kernel
-    holds at 32 keys per thread (host logic; no launches)."""
+    holds at 32 keys per thread; with multi-row blocks, only when some of
+    their rows is longer than the one-pass kernel holds at all (host logic;
+    no launches)."""
     from sparse_attention_decode_02_amd.step import ONE_PASS_RESIDENT_KEYS, histogram_topk_pays
     assert ONE_PASS_RESIDENT_KEYS == 32768
     req, ln = lib.plan_rows(np.array([65535, 2000, 40], np.int32), np.array([1, 1, 1], np.int32))
@@ -100,6 +102,14 @@ def test_histogram_topk_automatic_choice():
     assert not histogram_topk_pays(lib.plan_blocks(req3, 8), ln3, True)  # a prefill block
     assert histogram_topk_pays(lib.plan_blocks(req3, 1), ln3, True)      # rows scored alone
     assert not histogram_topk_pays(None, ln[:0], True)               # no rows
+    # prefill blocks of rows beyond 65536 keys (two-stage territory)
+    req4, ln4 = lib.plan_rows(np.array([65533, 200], np.int32), np.array([4, 1], np.int32))
+    assert int(ln4[:4].max()) == 65537
+    assert histogram_topk_pays(lib.plan_blocks(req4, 8), ln4, False)
+    assert histogram_topk_pays(lib.plan_blocks(req4, 8), ln4, True)
+    req5, ln5 = lib.plan_rows(np.array([65532], np.int32), np.array([4], np.int32))
+    assert int(ln5.max()) == 65536
+    assert not histogram_topk_pays(lib.plan_blocks(req5, 8), ln5, False)  # fits one pass
 
 
 def test_score_width():

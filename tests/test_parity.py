@@ -467,7 +467,9 @@ def test_step_automatic_histogram_topk():
     """With a row longer than the one-pass top-k holds at 32 keys per thread
     and no prefill blocks, the step's automatic choice takes the histogram
     selection, and it gives the one-pass step's indices and outputs bit for
-    bit (and the oracle's on the long row)."""
+    bit (and the oracle's on the long row); with prefill blocks only when
+    their rows are longer than the one-pass top-k holds at all (then the
+    two-stage step's bits)."""
     wl = I.custom(I.decode(), name="long_row", hq=16, hkv=2, topk=256,
                   prior=(40000, 300, 5000), new=(1, 1, 1), seed=29)
     inp = _host_inputs(wl)
@@ -482,6 +484,19 @@ def test_step_automatic_histogram_topk():
     # with a prefill block the automatic choice keeps the one-pass selection
     blk = DsaStep(_host_inputs(_small_mixed(seed=29)), block_rows=8, hist=None, topk_chunk=None)
     assert not blk.use_hist
+    # ... unless a block's rows are longer than the one-pass kernel holds:
+    # then the histogram selection replaces the two-stage one, same bits
+    wl2 = I.custom(I.decode(), name="long_block", hq=16, hkv=2, topk=256,
+                   prior=(65600, 300), new=(3, 1), seed=31)
+    inp2 = _host_inputs(wl2)
+    two = run_step(inp2, num_splits=4, block_rows=8, topk_chunk=32768)
+    outs2 = [t.clone() for t in (two.idx, two.out, two.out_lse)]
+    auto = run_step(inp2, num_splits=4, block_rows=8, hist=None, topk_chunk=None)
+    _say(f"automatic top-k, long prefill block: histogram {auto.use_hist}, chunk {auto.topk_chunk}")
+    assert auto.use_hist and not auto.topk_chunk
+    for a, b in zip(outs2, (auto.idx, auto.out, auto.out_lse)):
+        assert torch.equal(a.view(torch.uint8), b.view(torch.uint8))
+    check_row(auto, 1)
 
 
 def test_windowed_fp32_tiny():
