@@ -75,12 +75,13 @@ hipError_t indexer_launch(const void* q_idx, const float* w, const void* k_idx_c
                           const int32_t* row_len, const int32_t* blocks, int num_blocks,
                           float* scores, int rows, int width, int num_heads, int head_dim,
                           int page_shift, int max_pages, dsa_dtype dtype, bool full,
-                          hipStream_t st, int score_row0 = 0, uint32_t* hist = nullptr) {
+                          hipStream_t st, int score_row0 = 0, uint32_t* hist = nullptr,
+                          long long total_keys = 0) {
   const int nb = blocks ? num_blocks : rows;
   if (dtype == DSA_BF16)
     return dsa::launch_indexer_bf16(q_idx, w, k_idx_cache, block_table, row_req, row_len, blocks,
                                     nb, rows, scores, width, num_heads, head_dim, page_shift,
-                                    max_pages, full, score_row0, st, hist);
+                                    max_pages, full, score_row0, st, hist, total_keys);
   hipError_t e = dsa::launch_indexer_f32(static_cast<const float*>(q_idx), w,
                                          static_cast<const float*>(k_idx_cache), block_table,
                                          row_req, row_len, blocks, nb, scores, width, num_heads,
@@ -180,7 +181,7 @@ int dsa_indexer_scores_total(const void* q_idx, const float* w, const void* k_id
   return launch_status(indexer_launch(q_idx, w, k_idx_cache, block_table, row_req, row_len,
                                       blocks, num_blocks, scores, rows, width, num_heads,
                                       head_dim, ps, max_pages, dtype, full,
-                                      static_cast<hipStream_t>(stream)));
+                                      static_cast<hipStream_t>(stream), 0, nullptr, total_keys));
 }
 
 int dsa_indexer_scores_hist(const void* q_idx, const float* w, const void* k_idx_cache,
@@ -202,7 +203,7 @@ int dsa_indexer_scores_hist(const void* q_idx, const float* w, const void* k_idx
   return launch_status(indexer_launch(q_idx, w, k_idx_cache, block_table, row_req, row_len,
                                       blocks, num_blocks, scores, rows, width, num_heads,
                                       head_dim, ps, max_pages, dtype, full,
-                                      static_cast<hipStream_t>(stream), 0, hist));
+                                      static_cast<hipStream_t>(stream), 0, hist, total_keys));
 }
 
 int dsa_indexer_scores(const void* q_idx, const float* w, const void* k_idx_cache,

@@ -49,7 +49,7 @@ hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kc
                                const int32_t* blocks, int num_blocks, int rows, float* scores,
                                int width, int num_heads, int head_dim, int page_shift,
                                int max_pages, bool full, int score_row0, hipStream_t stream,
-                               uint32_t* hist = nullptr);
+                               uint32_t* hist = nullptr, long long total_keys = 0);
 
 hipError_t launch_indexer_f32(const float* q_idx, const float* w, const float* kcache,
                               const int32_t* bt, const int32_t* row_req, const int32_t* row_len,

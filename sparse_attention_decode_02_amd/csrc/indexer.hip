@@ -74,7 +74,7 @@ __device__ __forceinline__ float sum_rows(float x) {
 // columns. The k index of step kk, lane group g = l/16, element e is dim
 // kk*32 + g*8 + e for both operands, so the four lanes of a key read 64
 // contiguous bytes of its row per step.
-template <int HT, int DI>
+template <int HT, int DI, bool BAL = false>
 __global__ __launch_bounds__(kIdxThreads, 4) void indexer_mfma_kernel(
     const uint16_t* __restrict__ qI, const float* __restrict__ w,
     const uint16_t* __restrict__ kc, const int32_t* __restrict__ bt,
@@ -91,22 +91,56 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_mfma_kernel(
   __shared__ uint32_t h_lds[kHistBins / 2];
   __shared__ __attribute__((aligned(16))) float w_lds[H];
   __shared__ __attribute__((aligned(16))) float s_lds[kMaxChunkKeys];  // the chunk's scores
+  __shared__ uint32_t bal_sh[kIdxThreads / 64];
+  __shared__ int bal_item;
 
-  // Beside the block kernel only some blocks are this kernel's, so its
-  // items are dealt round-robin over the XCDs; alone, consecutive items
-  // (the chunks of a row) share an XCD, which measures faster for ragged
-  // batches.
-  const int item = single_only ? xcd_grouped<2>(blockIdx.x) : xcd_contiguous(blockIdx.x, total);
-  if (item >= total) return;
+  const int tid = threadIdx.x;
+  // Items are (block, chunk) pairs. Beside the block kernel only some blocks
+  // are this kernel's, so its items are dealt round-robin over the XCDs;
+  // alone, consecutive items (the chunks of a row) share an XCD, each XCD
+  // taking an equal range of (block, chunk) slots. A batch of ragged one-row
+  // blocks (BAL: at most one block per thread) would load the XCDs
+  // unevenly that way (a range holds whole rows), so there the active items
+  // -- chunks that start inside their row -- are numbered in row order,
+  // each XCD takes an equal contiguous share of them (workgroup i runs on
+  // XCD i % 8), and workgroup j of an XCD's J takes items j, j + J, ... of
+  // its share: any grid covers every item.
+  int kbeg, kend, kstep = 1;
+  uint32_t bal_pre = 0, bal_cnt = 0;  // BAL: thread t's block's first item and count
+  if constexpr (BAL) {
+    const int nb = total / chunks;
+    if (tid < nb) {
+      const int L = row_len[blocks ? blocks[2 * tid] : tid];
+      bal_cnt = L > 0 ? (uint32_t)min((L + chunk_keys - 1) / chunk_keys, chunks) : 0u;
+    }
+    uint32_t na;
+    bal_pre = block_exclusive_scan<kIdxThreads / 64>(bal_cnt, bal_sh, &na);
+    const int n = (int)na, x = (int)(blockIdx.x & 7), q = n >> 3, rem = n & 7;
+    const int start = x < rem ? x * (q + 1) : rem * (q + 1) + (x - rem) * q;
+    kbeg = start + (int)(blockIdx.x >> 3);
+    kend = start + (x < rem ? q + 1 : q);
+    kstep = (int)(gridDim.x >> 3);
+  } else {
+    kbeg = single_only ? xcd_grouped<2>(blockIdx.x) : xcd_contiguous(blockIdx.x, total);
+    kend = min(kbeg + 1, total);
+  }
+  for (int k = kbeg; k < kend; k += kstep) {
+  int item = k;
+  if constexpr (BAL) {
+    __syncthreads();  // every thread has read the previous item
+    if (bal_cnt > 0u && bal_pre <= (uint32_t)k && (uint32_t)k < bal_pre + bal_cnt)
+      bal_item = (int)tid * chunks + (k - (int)bal_pre);
+    __syncthreads();
+    item = bal_item;
+  }
   const int b = item / chunks;
   const int chunk0 = (item - b * chunks) * chunk_keys;
   int first = b, nrows = 1;
   if (blocks) {
     first = blocks[2 * b];
     nrows = blocks[2 * b + 1];
-    if (single_only && nrows > 1) return;  // the block kernel's
+    if (single_only && nrows > 1) continue;  // the block kernel's
   }
-  const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int kl = lane & 15, grp = lane >> 4;
   const int page_mask = (1 << page_shift) - 1;
@@ -242,6 +276,7 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_mfma_kernel(
         if (n >> 16) atomicAdd(&hr[2 * i + 1], n >> 16);
       }
     }
+  }
   }
 }
 
@@ -526,7 +561,7 @@ hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kc
                                const int32_t* blocks, int num_blocks, int rows, float* scores,
                                int width, int num_heads, int head_dim, int page_shift,
                                int max_pages, bool full, int score_row0, hipStream_t stream,
-                               uint32_t* hist) {
+                               uint32_t* hist, long long total_keys) {
   const auto* q = static_cast<const uint16_t*>(q_idx);
   const auto* k = static_cast<const uint16_t*>(kcache);
   const bool with_block_kernel = blocks && indexer_uses_blocks(rows, num_blocks);
@@ -548,13 +583,30 @@ hipError_t launch_indexer_bf16(const void* q_idx, const float* w, const void* kc
     const int chunk = indexer_chunk_keys(num_blocks, width, num_heads, head_dim, full);
     const int chunks = (width + chunk - 1) / chunk;
     const int total = num_blocks * chunks;
+    int grid = single_only ? xcd_grouped_grid(total, 2) : total;
+    // Ragged batches of one-row blocks balance their active items over the
+    // XCDs; the row plan's key count sizes the grid (one item a workgroup
+    // when it is right: each row has at most one partial chunk), and the
+    // workgroups loop over their share if it is not.
+    const bool balanced =
+        !with_block_kernel && !full && total_keys > 0 && num_blocks == rows && rows <= kIdxThreads;
+    if (balanced) {
+      const long long bound = std::min<long long>(total, total_keys / chunk + num_blocks);
+      grid = (int)((bound + 7) / 8 * 8);
+    }
 #define DSA_IDX_LAUNCH(HT, DI)                                                                 \
-  hipLaunchKernelGGL((indexer_mfma_kernel<HT, DI>),                                            \
-                     dim3(single_only ? xcd_grouped_grid(total, 2) : total), dim3(kIdxThreads), 0, \
-                     row_stream,                                                               \
-                     q, w, k, bt, row_req, row_len, blocks, scores, width, page_shift,         \
-                     max_pages, chunk, chunks, total, score_row0, single_only,                 \
-                     with_block_kernel ? nullptr : hist)
+  do {                                                                                         \
+    if (balanced)                                                                              \
+      hipLaunchKernelGGL((indexer_mfma_kernel<HT, DI, true>), dim3(grid), dim3(kIdxThreads), 0, \
+                         row_stream, q, w, k, bt, row_req, row_len, blocks, scores, width,     \
+                         page_shift, max_pages, chunk, chunks, total, score_row0, single_only, \
+                         with_block_kernel ? nullptr : hist);                                  \
+    else                                                                                       \
+      hipLaunchKernelGGL((indexer_mfma_kernel<HT, DI>), dim3(grid), dim3(kIdxThreads), 0,      \
+                         row_stream, q, w, k, bt, row_req, row_len, blocks, scores, width,     \
+                         page_shift, max_pages, chunk, chunks, total, score_row0, single_only, \
+                         with_block_kernel ? nullptr : hist);                                  \
+  } while (0)
     if (num_heads == 64 && head_dim == 128) DSA_IDX_LAUNCH(4, 128);
     else if (num_heads == 32 && head_dim == 128) DSA_IDX_LAUNCH(2, 128);
     else if (num_heads == 64 && head_dim == 64) DSA_IDX_LAUNCH(4, 64);

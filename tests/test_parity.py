@@ -835,15 +835,25 @@ def test_graph_replay_matches_eager(fused, block_rows):
         check_row(step, r)
 
 
-@pytest.mark.parametrize("wl_fn", [I.decode, lambda: _small_mixed(seed=31)], ids=["decode", "small-mixed"])
+def _ragged_rows(seed=43):
+    """Twelve decode rows from 1 to 40001 keys: many 1024-key chunks, unevenly."""
+    prior = (40000, 0, 300, 9000, 25000, 4095, 17, 12000, 1023, 1024, 30000, 6)
+    return I.custom(I.decode(), name="ragged_rows", hq=16, hkv=2, topk=256, prior=prior,
+                    new=(1,) * len(prior), seed=seed)
+
+
+@pytest.mark.parametrize("wl_fn", [I.decode, lambda: _small_mixed(seed=31), _ragged_rows],
+                         ids=["decode", "small-mixed", "ragged"])
 def test_indexer_hint_keeps_scores(wl_fn):
-    """The total-keys hint (larger key chunks for rows that fill the width)
-    changes the launch shape, never a score bit."""
+    """The total-keys hint (larger key chunks for rows that fill the width;
+    for ragged one-row batches, a grid of about one workgroup per active
+    chunk, balanced over the XCDs) changes the launch shape, never a score
+    bit: a hint below the true count makes workgroups take several chunks."""
     from sparse_attention_decode_02_amd import lib
     step = run_step(_host_inputs(wl_fn()))
     i = step.inp
     ref = step.scores.clone()
-    for total in (0, step.total_keys, step.rows * step.width):
+    for total in (0, 1, step.total_keys // 3, step.total_keys, step.rows * step.width):
         step.scores.view(torch.int32).fill_(CANARY)
         lib.indexer_scores(i.qI, i.w, i.kI_cache, i.block_table, step.row_req, step.row_len,
                            step.scores, step.wl.page, total_keys=total)
