@@ -304,11 +304,15 @@ __global__ __launch_bounds__(kGaThreads, 4) void group_attn_kernel(
     }
     __syncthreads();
     // Every entry's cache row through the block table at once (one round
-    // trip per window instead of a dependent lookup per tile).
+    // trip per window instead of a dependent lookup per tile); the mask
+    // bytes past the union up to the last tile's end are cleared, so those
+    // slots select no row.
     for (int e = tid; e < (int)n_u; e += kGaThreads) {
       const int p = (int)urow[e];
       urow[e] = ((uint32_t)btr[p >> page_shift] << page_shift) | (uint32_t)(p & page_mask);
     }
+    for (int e = (int)n_u + tid; e < (((int)n_u + kGaTile - 1) & ~(kGaTile - 1)); e += kGaThreads)
+      umask[e] = 0u;
     __syncthreads();
 
     // ---- tiles of the window's union ----
@@ -344,28 +348,29 @@ __global__ __launch_bounds__(kGaThreads, 4) void group_attn_kernel(
         }
       }
       // Mask: the four union entries e0 + n * 16 + 4 (l / 16) .. + 3 in one
-      // word of the byte map, bit my_tr of each.
-      float x[2][4];
-      bool over = false;
+      // word of the byte map, bit my_tr of each (slots past the union hold
+      // no bits); a masked key scores -inf.
+      bool ok[2][4];
+      float sv[2][4];
 #pragma unroll
       for (int n = 0; n < 2; ++n) {
-        const int eb = e0 + n * 16 + 4 * kgrp;
-        const uint32_t mw = *reinterpret_cast<const uint32_t*>(umask + eb) >> my_tr;
+        const uint32_t mw = *reinterpret_cast<const uint32_t*>(umask + e0 + n * 16 + 4 * kgrp) >> my_tr;
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const bool ok = eb + i < (int)n_u && ((mw >> (8 * i)) & 1u);
-          x[n][i] = ok ? s[n][i] * scale_log2 : -INFINITY;
-          over |= x[n][i] > m + kGaSlack;
+          ok[n][i] = (mw >> (8 * i)) & 1u;
+          sv[n][i] = ok[n][i] ? s[n][i] : -INFINITY;
         }
       }
-      // Online softmax against a deferred reference: a row's m is raised to
-      // its running max (and its sum and outputs rescaled) only when a score
-      // overtakes it by more than 2^kGaSlack, so most tiles skip the
-      // rescale; o and the sum share the reference, so the normalized
-      // result is the same and every probability stays <= 2^kGaSlack.
-      if (__ballot(over) != 0) {
-        float xm = fmaxf(fmaxf(x[0][0], x[0][1]), fmaxf(x[0][2], x[0][3]));
-        xm = fmaxf(xm, fmaxf(fmaxf(x[1][0], x[1][1]), fmaxf(x[1][2], x[1][3])));
+      // Online softmax in base 2 (x = s * scale_log2) against a deferred
+      // reference: a row's m is raised to its running max (and its sum and
+      // outputs rescaled) only when a score overtakes it by more than
+      // 2^kGaSlack, so most tiles skip the rescale; o and the sum share the
+      // reference, so the normalized result is the same and every
+      // probability stays <= 2^kGaSlack. The lane's largest x is its largest
+      // s times the (positive) scale: rounding keeps the order.
+      float xm = fmaxf(fmaxf(sv[0][0], sv[0][1]), fmaxf(sv[0][2], sv[0][3]));
+      xm = fmaxf(xm, fmaxf(fmaxf(sv[1][0], sv[1][1]), fmaxf(sv[1][2], sv[1][3]))) * scale_log2;
+      if (__ballot(xm > m + kGaSlack) != 0) {
         const float mt = groups4_max(xm);
         const bool up = mt > m + kGaSlack;
         // m = -inf (no selected key yet): alpha = 0 clears what is zero.
@@ -385,7 +390,7 @@ __global__ __launch_bounds__(kGaThreads, 4) void group_attn_kernel(
       for (int n = 0; n < 2; ++n)
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const float p = x[n][i] == -INFINITY ? 0.0f : __builtin_amdgcn_exp2f(x[n][i] - m);
+          const float p = ok[n][i] ? __builtin_amdgcn_exp2f(fmaf(s[n][i], scale_log2, -m)) : 0.0f;
           ps += p;
           const uint32_t u0 = __float_as_uint(p);
           const float r1 = p - __uint_as_float(u0 & 0xFFFF0000u);  // exact
