@@ -149,9 +149,13 @@ int dsa_indexer_scores(const void* q_idx, const float* w, const void* k_idx_cach
 /* dsa_indexer_scores with a scheduling hint: total_keys = the sum of row_len
  * over the rows (known on the host from the row plan; 0 = unknown). Rows that
  * fill at least 90% of rows x width are scored in larger key chunks (no
- * ragged tail to balance). The scores are identical either way; the launch
- * shape depends only on the arguments, so a replayed step must pass the same
- * hint. total_keys outside [0, rows * width]: DSA_ERR_SHAPE. */
+ * ragged tail to balance); a ragged batch of at most 256 rows in one-row
+ * blocks spreads the key chunks its rows actually hold evenly over the
+ * XCDs, with the grid sized from the hint (a hint below the true sum only
+ * makes workgroups take several chunks). The scores are identical either
+ * way; the launch shape depends only on the arguments, so a replayed step
+ * must pass the same hint. total_keys outside [0, rows * width]:
+ * DSA_ERR_SHAPE. */
 int dsa_indexer_scores_total(const void* q_idx, const float* w, const void* k_idx_cache,
                              const int32_t* block_table, const int32_t* row_req,
                              const int32_t* row_len, const int32_t* blocks, int num_blocks,
