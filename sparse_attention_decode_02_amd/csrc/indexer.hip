@@ -125,158 +125,160 @@ __global__ __launch_bounds__(kIdxThreads, 4) void indexer_mfma_kernel(
     kend = min(kbeg + 1, total);
   }
   for (int k = kbeg; k < kend; k += kstep) {
-  int item = k;
-  if constexpr (BAL) {
-    __syncthreads();  // every thread has read the previous item
-    if (bal_cnt > 0u && bal_pre <= (uint32_t)k && (uint32_t)k < bal_pre + bal_cnt)
-      bal_item = (int)tid * chunks + (k - (int)bal_pre);
-    __syncthreads();
-    item = bal_item;
-  }
-  const int b = item / chunks;
-  const int chunk0 = (item - b * chunks) * chunk_keys;
-  int first = b, nrows = 1;
-  if (blocks) {
-    first = blocks[2 * b];
-    nrows = blocks[2 * b + 1];
-    if (single_only && nrows > 1) continue;  // the block kernel's
-  }
-  const int lane = tid & 63, wave = tid >> 6;
-  const int kl = lane & 15, grp = lane >> 4;
-  const int page_mask = (1 << page_shift) - 1;
-
-  // Wave-uniform pieces (readfirstlane makes them SGPRs, so the page lookups
-  // below are scalar loads: they wait on the scalar counter and never on the
-  // key loads still in flight).
-  const int wv = __builtin_amdgcn_readfirstlane(wave);
-  constexpr int kStep = 4 * kTileKeys;  // the workgroup's 4 waves interleave tiles
-  constexpr int QV = H * DI / 8 / kIdxThreads;  // uint4 of the query block per thread
-  static_assert(QV * kIdxThreads * 8 == H * DI, "query block must split evenly over the threads");
-
-  for (int rr = 0; rr < nrows; ++rr) {
-    const int r = first + rr;
-    const int L = row_len[r];
-    if (chunk0 >= L) continue;  // uniform over the workgroup
-    const int req = row_req[r];
-    const int32_t* btr = bt + (size_t)req * max_pages;
-    const int end = min(L, chunk0 + chunk_keys);
-    float* out = scores + (size_t)(r - score_row0) * width;  // rows of a window from its first
-
-    // Key fragments of the 16-key tile at `base` (base is wave-uniform). The
-    // tile lies inside one page (page size >= 16), whose number is one scalar
-    // load. Loads are unconditional -- positions past the workgroup's chunk
-    // re-read its last key (a cache hit) and are never stored -- so the load
-    // counter stays exact and a prefetch is never waited on early.
-    auto load_tile = [&](int base, bf16x8 (&kf)[KS]) {
-      const int page = btr[min(base, end - 1) >> page_shift];
-      const int s = min(base + kl, end - 1);
-      const size_t krow = ((size_t)page << page_shift) | (size_t)(s & page_mask);
-      const bf16x8* p = reinterpret_cast<const bf16x8*>(kc + krow * DI + grp * 8);
-#pragma unroll
-      for (int kk = 0; kk < KS; ++kk) kf[kk] = p[kk * 4];
-    };
-
-    // Prologue: the first key tiles, then the query block and head weights,
-    // all in flight together; one wait covers them before the query goes to
-    // LDS.
-    const int base0 = chunk0 + wv * kTileKeys;
-    const int ntiles = (end - base0 + kStep - 1) / kStep;  // this wave's tiles (may be <= 0)
-    bf16x8 kbuf[kKeyBufs][KS];
-#pragma unroll
-    for (int i = 0; i < kKeyBufs - 1; ++i) load_tile(base0 + i * kStep, kbuf[i]);
-    __syncthreads();  // the previous row's readers are done with q_lds / w_lds
-    {
-      const uint4* src = reinterpret_cast<const uint4*>(qI + (size_t)r * H * DI);
-      uint4 qreg[QV];
-#pragma unroll
-      for (int i = 0; i < QV; ++i) qreg[i] = src[tid + i * kIdxThreads];
-      const float wv_ = tid < H ? w[(size_t)r * H + tid] : 0.0f;
-#pragma unroll
-      for (int i = 0; i < QV; ++i) {
-        const int e = tid + i * kIdxThreads;
-        const int h = e / (DI / 8), c = e - h * (DI / 8);
-        *reinterpret_cast<uint4*>(&q_lds[h * QST + c * 8]) = qreg[i];
-      }
-      if (tid < H) w_lds[tid] = wv_;
-      if (hist)
-        for (int i = tid; i < kHistBins / 2; i += kIdxThreads) h_lds[i] = 0u;
+    int item = k;
+    if constexpr (BAL) {
+      __syncthreads();  // every thread has read the previous item
+      if (bal_cnt > 0u && bal_pre <= (uint32_t)k && (uint32_t)k < bal_pre + bal_cnt)
+        bal_item = (int)tid * chunks + (k - (int)bal_pre);
+      __syncthreads();
+      item = bal_item;
     }
-    __syncthreads();
+    const int b = item / chunks;
+    const int chunk0 = (item - b * chunks) * chunk_keys;
+    int first = b, nrows = 1;
+    if (blocks) {
+      first = blocks[2 * b];
+      nrows = blocks[2 * b + 1];
+      if (single_only && nrows > 1) continue;  // the block kernel's
+    }
+    const int lane = tid & 63, wave = tid >> 6;
+    const int kl = lane & 15, grp = lane >> 4;
+    const int page_mask = (1 << page_shift) - 1;
 
-    float4 wr[HT];
-#pragma unroll
-    for (int t = 0; t < HT; ++t) wr[t] = *reinterpret_cast<const float4*>(&w_lds[t * 16 + grp * 4]);
-    const int qoff0 = kl * QST + grp * 8;
+    // Wave-uniform pieces (readfirstlane makes them SGPRs, so the page lookups
+    // below are scalar loads: they wait on the scalar counter and never on the
+    // key loads still in flight).
+    const int wv = __builtin_amdgcn_readfirstlane(wave);
+    constexpr int kStep = 4 * kTileKeys;  // the workgroup's 4 waves interleave tiles
+    constexpr int QV = H * DI / 8 / kIdxThreads;  // uint4 of the query block per thread
+    static_assert(QV * kIdxThreads * 8 == H * DI, "query block must split evenly over the threads");
 
-    auto score_tile = [&](int base, const bf16x8 (&kf)[KS]) {
-      // The empty asm makes the LDS offset opaque, so the compiler cannot hoist
-      // the query reads out of the tile loop into registers.
-      int qoff = qoff0;
-      asm volatile("" : "+v"(qoff));
-      float part = 0.0f;
-#pragma unroll
-      for (int t = 0; t < HT; ++t) {
-        f32x4 acc = {};
-#pragma unroll
-        for (int kk = 0; kk < KS; ++kk) {
-          const bf16x8 qv = *reinterpret_cast<const bf16x8*>(&q_lds[t * 16 * QST + kk * 32 + qoff]);
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qv, kf[kk], acc, 0, 0, 0);
+    for (int rr = 0; rr < nrows; ++rr) {
+      const int r = first + rr;
+      const int L = row_len[r];
+      if (chunk0 >= L) continue;  // uniform over the workgroup
+      const int req = row_req[r];
+      const int32_t* btr = bt + (size_t)req * max_pages;
+      const int end = min(L, chunk0 + chunk_keys);
+      float* out = scores + (size_t)(r - score_row0) * width;  // rows of a window from its first
+
+      // Key fragments of the 16-key tile at `base` (base is wave-uniform). The
+      // tile lies inside one page (page size >= 16), whose number is one scalar
+      // load. Loads are unconditional -- positions past the workgroup's chunk
+      // re-read its last key (a cache hit) and are never stored -- so the load
+      // counter stays exact and a prefetch is never waited on early.
+      auto load_tile = [&](int base, bf16x8 (&kf)[KS]) {
+        const int page = btr[min(base, end - 1) >> page_shift];
+        const int s = min(base + kl, end - 1);
+        const size_t krow = ((size_t)page << page_shift) | (size_t)(s & page_mask);
+        const bf16x8* p = reinterpret_cast<const bf16x8*>(kc + krow * DI + grp * 8);
+  #pragma unroll
+        for (int kk = 0; kk < KS; ++kk) kf[kk] = p[kk * 4];
+      };
+
+      // Prologue: the first key tiles, then the query block and head weights,
+      // all in flight together; one wait covers them before the query goes to
+      // LDS.
+      const int base0 = chunk0 + wv * kTileKeys;
+      const int ntiles = (end - base0 + kStep - 1) / kStep;  // this wave's tiles (may be <= 0)
+      bf16x8 kbuf[kKeyBufs][KS];
+  #pragma unroll
+      for (int i = 0; i < kKeyBufs - 1; ++i) load_tile(base0 + i * kStep, kbuf[i]);
+      __syncthreads();  // the previous row's readers are done with q_lds / w_lds
+      {
+        const uint4* src = reinterpret_cast<const uint4*>(qI + (size_t)r * H * DI);
+        uint4 qreg[QV];
+  #pragma unroll
+        for (int i = 0; i < QV; ++i) qreg[i] = src[tid + i * kIdxThreads];
+        const float wv_ = tid < H ? w[(size_t)r * H + tid] : 0.0f;
+  #pragma unroll
+        for (int i = 0; i < QV; ++i) {
+          const int e = tid + i * kIdxThreads;
+          const int h = e / (DI / 8), c = e - h * (DI / 8);
+          *reinterpret_cast<uint4*>(&q_lds[h * QST + c * 8]) = qreg[i];
         }
-        part = fmaf(wr[t].x, relu(acc[0]), part);
-        part = fmaf(wr[t].y, relu(acc[1]), part);
-        part = fmaf(wr[t].z, relu(acc[2]), part);
-        part = fmaf(wr[t].w, relu(acc[3]), part);
+        if (tid < H) w_lds[tid] = wv_;
+        if (hist)
+          for (int i = tid; i < kHistBins / 2; i += kIdxThreads) h_lds[i] = 0u;
       }
-      part = sum_rows(part) + 0.0f;
-      const int s = base + kl;
-      if (grp == 0 && s < L) {
-        s_lds[s - chunk0] = part;
-        if (hist) {
-          // Counted as it is made, under the key loads in flight.
-          const uint32_t bin = order_key(part) >> kHistShift;
-          atomicAdd(&h_lds[bin >> 1], 1u << ((bin & 1u) << 4));
+      __syncthreads();
+
+      float4 wr[HT];
+  #pragma unroll
+      for (int t = 0; t < HT; ++t)
+        wr[t] = *reinterpret_cast<const float4*>(&w_lds[t * 16 + grp * 4]);
+      const int qoff0 = kl * QST + grp * 8;
+
+      auto score_tile = [&](int base, const bf16x8 (&kf)[KS]) {
+        // The empty asm makes the LDS offset opaque, so the compiler cannot hoist
+        // the query reads out of the tile loop into registers.
+        int qoff = qoff0;
+        asm volatile("" : "+v"(qoff));
+        float part = 0.0f;
+  #pragma unroll
+        for (int t = 0; t < HT; ++t) {
+          f32x4 acc = {};
+  #pragma unroll
+          for (int kk = 0; kk < KS; ++kk) {
+            const bf16x8 qv =
+                *reinterpret_cast<const bf16x8*>(&q_lds[t * 16 * QST + kk * 32 + qoff]);
+            acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qv, kf[kk], acc, 0, 0, 0);
+          }
+          part = fmaf(wr[t].x, relu(acc[0]), part);
+          part = fmaf(wr[t].y, relu(acc[1]), part);
+          part = fmaf(wr[t].z, relu(acc[2]), part);
+          part = fmaf(wr[t].w, relu(acc[3]), part);
+        }
+        part = sum_rows(part) + 0.0f;
+        const int s = base + kl;
+        if (grp == 0 && s < L) {
+          s_lds[s - chunk0] = part;
+          if (hist) {
+            // Counted as it is made, under the key loads in flight.
+            const uint32_t bin = order_key(part) >> kHistShift;
+            atomicAdd(&h_lds[bin >> 1], 1u << ((bin & 1u) << 4));
+          }
+        }
+      };
+
+      // kKeyBufs key-fragment buffers in rotation: while one tile runs on the
+      // matrix cores the next two are in flight. The trip count is fixed and
+      // every load unconditional, so each wait covers exactly the tile in use.
+      for (int it = 0; it < ntiles; it += kKeyBufs) {
+  #pragma unroll
+        for (int u = 0; u < kKeyBufs; ++u) {
+          const int cur = base0 + (it + u) * kStep;
+          load_tile(cur + (kKeyBufs - 1) * kStep, kbuf[(u + kKeyBufs - 1) % kKeyBufs]);
+          if (it + u < ntiles) score_tile(cur, kbuf[u]);
         }
       }
-    };
-
-    // kKeyBufs key-fragment buffers in rotation: while one tile runs on the
-    // matrix cores the next two are in flight. The trip count is fixed and
-    // every load unconditional, so each wait covers exactly the tile in use.
-    for (int it = 0; it < ntiles; it += kKeyBufs) {
-#pragma unroll
-      for (int u = 0; u < kKeyBufs; ++u) {
-        const int cur = base0 + (it + u) * kStep;
-        load_tile(cur + (kKeyBufs - 1) * kStep, kbuf[(u + kKeyBufs - 1) % kKeyBufs]);
-        if (it + u < ntiles) score_tile(cur, kbuf[u]);
+      // The chunk's scores leave in whole lines with streaming stores once the
+      // chunk is done: writing each tile's 16 scores as they come costs a few
+      // percent of the kernel's time against the key reads.
+      __syncthreads();
+      typedef float f32x4v __attribute__((ext_vector_type(4)));
+      const int nk = end - chunk0;
+      for (int i = tid * 4; i < nk; i += kIdxThreads * 4) {
+        if (i + 4 <= nk) {
+          __builtin_nontemporal_store(*reinterpret_cast<const f32x4v*>(&s_lds[i]),
+                                      reinterpret_cast<f32x4v*>(out + chunk0 + i));
+        } else {
+          for (int j = i; j < nk; ++j) out[chunk0 + j] = s_lds[j];
+        }
+      }
+      if (hist) {
+        // The chunk's counts (the selection's threshold histogram: scores by
+        // the top 12 bits of their order keys) join the row's: one global
+        // atomic per non-empty bin. The next row clears h_lds only after a
+        // barrier.
+        uint32_t* hr = hist + (size_t)(r - score_row0) * kHistBins;
+        for (int i = tid; i < kHistBins / 2; i += kIdxThreads) {
+          const uint32_t n = h_lds[i];
+          if (n & 0xFFFFu) atomicAdd(&hr[2 * i], n & 0xFFFFu);
+          if (n >> 16) atomicAdd(&hr[2 * i + 1], n >> 16);
+        }
       }
     }
-    // The chunk's scores leave in whole lines with streaming stores once the
-    // chunk is done: writing each tile's 16 scores as they come costs a few
-    // percent of the kernel's time against the key reads.
-    __syncthreads();
-    typedef float f32x4v __attribute__((ext_vector_type(4)));
-    const int nk = end - chunk0;
-    for (int i = tid * 4; i < nk; i += kIdxThreads * 4) {
-      if (i + 4 <= nk) {
-        __builtin_nontemporal_store(*reinterpret_cast<const f32x4v*>(&s_lds[i]),
-                                    reinterpret_cast<f32x4v*>(out + chunk0 + i));
-      } else {
-        for (int j = i; j < nk; ++j) out[chunk0 + j] = s_lds[j];
-      }
-    }
-    if (hist) {
-      // The chunk's counts (the selection's threshold histogram: scores by
-      // the top 12 bits of their order keys) join the row's: one global
-      // atomic per non-empty bin. The next row clears h_lds only after a
-      // barrier.
-      uint32_t* hr = hist + (size_t)(r - score_row0) * kHistBins;
-      for (int i = tid; i < kHistBins / 2; i += kIdxThreads) {
-        const uint32_t n = h_lds[i];
-        if (n & 0xFFFFu) atomicAdd(&hr[2 * i], n & 0xFFFFu);
-        if (n >> 16) atomicAdd(&hr[2 * i + 1], n >> 16);
-      }
-    }
-  }
   }
 }
 
