@@ -267,6 +267,31 @@ def test_score_hist_matches_oracle(width):
         assert np.array_equal(got[i], _oracle_hist(sc, len(sc))), name
 
 
+def test_score_hist_counter_bound():
+    """dsa_score_hist at the largest count one of its 16-bit LDS counters can
+    take: 1024 rows of 62 x 8192 positions give two workgroups a row, each
+    counting 31 chunks, and rows of equal scores put all of a copy's keys in
+    one bin (64 threads x 32 keys x 31 = 63488); random rows beside them
+    match the oracle's histogram."""
+    from sparse_attention_decode_02_amd import lib
+    rows, width = 1024, 62 * 8192
+    scores = torch.ones(rows, width, dtype=torch.float32, device="cuda")
+    rng = np.random.default_rng(47)
+    rand = [rng.standard_normal(width).astype(np.float32) for _ in range(4)]
+    for i, sc in enumerate(rand):
+        scores[rows - 1 - i] = torch.from_numpy(sc).cuda()
+    lens = torch.full((rows,), width, dtype=torch.int32, device="cuda")
+    hist = torch.full((rows, lib.HIST_BINS), 7, dtype=torch.int32, device="cuda")
+    lib.score_hist(scores, lens, hist)
+    got = hist.cpu().numpy().astype(np.int64)
+    del scores
+    want = _oracle_hist(np.ones(1, np.float32), 1) * width
+    for r in range(rows - 4):
+        assert np.array_equal(got[r], want), r
+    for i, sc in enumerate(rand):
+        assert np.array_equal(got[rows - 1 - i], _oracle_hist(sc, width)), i
+
+
 @pytest.mark.parametrize("k", [1, 16, 2048])
 @pytest.mark.parametrize("copies,width", [(1, 70016), (13, 70016), (1, 4096), (1, 8192), (3, 16384)],
                          ids=["few-rows", "many-rows", "w4096", "w8192", "w16384"])
