@@ -615,23 +615,26 @@ def test_attention_padding_anywhere(S):
             assert float(np.abs(gl[fl] - wl_[fl]).max()) <= tol_l, r
 
 
-def _prefill_groups_wl(seed=51, topk=256):
+def _prefill_groups_wl(seed=51, topk=256, page=64):
     # Prefill chunks of 37, 9, 8 and 3 rows on short and long prior contexts
-    # (unions spanning several 4096-position windows), plus two decode rows;
-    # 64 query / 8 KV heads of dim 128 (8 heads per group).
+    # (unions spanning several of the kernel's 1024-position windows), plus
+    # two decode rows; 64 query / 8 KV heads of dim 128 (8 heads per group).
     prior = (700, 5000, 60, 0, 20000, 3000, 9)
     new = (37, 9, 8, 3, 6, 1, 1)
     return I.custom(I.decode(), name="prefill_groups", hq=64, hkv=8, topk=topk, prior=prior,
-                    new=new, seed=seed)
+                    new=new, seed=seed, page=page)
 
 
-@pytest.mark.parametrize("block_rows,topk", [(8, 256), (3, 256), (8, 2048), (1, 64)])
-def test_group_attn_matches_oracle(block_rows, topk):
+@pytest.mark.parametrize("block_rows,topk,page", [(8, 256, 64), (3, 256, 64), (8, 2048, 64),
+                                                  (1, 64, 64), (8, 256, 16), (5, 2048, 128)])
+def test_group_attn_matches_oracle(block_rows, topk, page):
     """dsa_group_attn (the union of a group's selections with per-row masks,
     matrix cores) writes every row's attention output and log-sum-exp within
-    the bf16 tolerances of the oracle, for groups of 1..8 rows."""
+    the bf16 tolerances of the oracle, for groups of 1..8 rows and pages of
+    16, 64 and 128 positions (each union entry's cache row comes through the
+    block table)."""
     from sparse_attention_decode_02_amd import lib
-    inp = _host_inputs(_prefill_groups_wl(topk=topk))
+    inp = _host_inputs(_prefill_groups_wl(topk=topk, page=page))
     step = run_step(inp, block_rows=1, num_splits=1)
     groups_host = lib.plan_blocks(step.row_req_host, block_rows)
     groups = torch.from_numpy(groups_host).cuda()
