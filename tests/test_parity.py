@@ -959,7 +959,10 @@ def _same_selection_other_ways(step):
 def _full(wl, rows_fn):
     _say(f"{wl.name}: generating on the device")
     inp = I.generate(wl, "cuda")
-    step = run_step(inp, fused=None, block_rows=8)  # the launch configuration bench.py times
+    # bench.py's launch configuration, with the one-pass or two-stage top-k;
+    # the histogram top-k it may take instead must give the same indices
+    # (checked in _same_selection_other_ways).
+    step = run_step(inp, fused=None, block_rows=8)
     _say(f"  rows {step.rows}, width {step.width}, splits {step.num_splits}")
     check_properties(step)
     _same_selection_other_ways(step)
